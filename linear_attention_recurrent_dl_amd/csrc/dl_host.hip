@@ -1,0 +1,404 @@
+// Host side of the DeltaLog C ABI (include/deltalog.h): pool descriptor
+// validation, buffer sizing, the host mirror of every slot's live-log length
+// (the append / merge schedule of [DL]'s append-merge cycle), slot
+// assignment, and kernel launches.
+//
+// [DL] = "DeltaLog: Deferred Materialization of Recurrent States for Linear
+// Attention Decoding".  The phase of a decoded slot follows its design
+// section: a slot whose log holds C = L - 1 entries takes the merge step,
+// any other appends at index n.  The serving-integration section's allocator
+// gives a fresh slot the supplied base and an empty log.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/deltalog.h"
+#include "dl_internal.hpp"
+
+namespace dl {
+template <int D>
+hipError_t launch_step_d(int, int, int, int, int, const StepParams &, size_t, hipStream_t);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DL_OK;
+}
+
+size_t dtype_size(int dt) { return dt == DL_BF16 ? 2 : 4; }
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int validate_desc(const dl_pool_desc *d) {
+    if (!d) return fail(DL_ERR_INVALID_ARG, "desc is NULL");
+    if (d->num_slots < 1) return fail(DL_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", d->num_slots);
+    if (d->max_batch < 1) return fail(DL_ERR_INVALID_ARG, "max_batch must be >= 1 (got %d)", d->max_batch);
+    if (d->num_v_heads < 1 || d->num_k_heads < 1)
+        return fail(DL_ERR_INVALID_ARG, "head counts must be >= 1 (H_v=%d, H_k=%d)", d->num_v_heads, d->num_k_heads);
+    if (d->num_v_heads % d->num_k_heads)
+        return fail(DL_ERR_INVALID_ARG, "num_v_heads (%d) must be a multiple of num_k_heads (%d)",
+                    d->num_v_heads, d->num_k_heads);
+    if (d->merge_interval < 1 || d->merge_interval > dl::kMaxLogCap + 1)
+        return fail(DL_ERR_INVALID_ARG, "merge_interval must be in [1, %d] (got %d)", dl::kMaxLogCap + 1,
+                    d->merge_interval);
+    if (d->decay < DL_DECAY_NONE || d->decay > DL_DECAY_PER_KEY) return fail(DL_ERR_INVALID_ARG, "bad decay %d", d->decay);
+    if (d->update < DL_UPDATE_PLAIN || d->update > DL_UPDATE_DELTA) return fail(DL_ERR_INVALID_ARG, "bad update %d", d->update);
+    if ((d->state_dtype != DL_F32 && d->state_dtype != DL_BF16) || (d->in_dtype != DL_F32 && d->in_dtype != DL_BF16))
+        return fail(DL_ERR_INVALID_ARG, "bad dtype (state %d, in %d)", d->state_dtype, d->in_dtype);
+    if (d->d_k != d->d_v || !supported_dim(d->d_k))
+        return fail(DL_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d not built (need d_k == d_v in {16,32,64,128})",
+                    d->d_k, d->d_v);
+    const long long units = (long long)d->max_batch * d->num_v_heads;
+    if (units > (1LL << 30)) return fail(DL_ERR_INVALID_ARG, "max_batch * num_v_heads too large");
+    return DL_OK;
+}
+
+void compute_sizes(const dl_pool_desc *d, size_t out[DL_NUM_BUFS]) {
+    const size_t P = d->num_slots, Hv = d->num_v_heads, Hk = d->num_k_heads, D = d->d_k;
+    const size_t C = d->merge_interval - 1;
+    const size_t b_size = d->update == DL_UPDATE_DELTA ? 4 : dtype_size(d->in_dtype);
+    const size_t lam_w = d->decay == DL_DECAY_PER_KEY ? D : 1;
+    out[DL_BUF_BASE] = P * Hv * D * D * dtype_size(d->state_dtype);
+    out[DL_BUF_KLOG] = P * Hk * C * D * dtype_size(d->in_dtype);
+    out[DL_BUF_ULOG] = P * Hv * C * D * b_size;
+    out[DL_BUF_LAMLOG] = d->decay == DL_DECAY_NONE ? 0 : P * Hv * C * lam_w * 4;
+    out[DL_BUF_NLOG] = P * Hv * 4;
+}
+
+__global__ void dl_zero_i32_kernel(int32_t *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Fresh-slot assignment: one block per (slot, v-head), 16-byte copies of the
+// given base (or zeros), then an empty log.
+__global__ void __launch_bounds__(256) dl_assign_kernel(const dl::AssignParams p) {
+    const int unit = blockIdx.x;
+    const int j = unit / p.H_v, h = unit - j * p.H_v;
+    const size_t sh = (size_t)p.slots[j] * p.H_v + h;
+    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(p.base) + sh * p.head_bytes);
+    const int64_t nvec = p.head_bytes / 16;
+    if (p.init) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.init) + (size_t)unit * p.head_bytes);
+        for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = src[i];
+    } else {
+        for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = make_uint4(0, 0, 0, 0);
+    }
+    if (threadIdx.x == 0) p.nlog[sh] = 0;
+}
+
+}  // namespace
+
+namespace dl {
+
+int block_threads(int D, int st) {
+    (void)st;
+    return D >= 128 ? 256 : (D >= 64 ? 128 : 64);
+}
+
+int launch_step(int D, int mode, int decay, int update, int st, int it, const StepParams &p, size_t shmem,
+                hipStream_t s) {
+    switch (D) {
+    case 16: return (int)launch_step_d<16>(mode, decay, update, st, it, p, shmem, s);
+    case 32: return (int)launch_step_d<32>(mode, decay, update, st, it, p, shmem, s);
+    case 64: return (int)launch_step_d<64>(mode, decay, update, st, it, p, shmem, s);
+    case 128: return (int)launch_step_d<128>(mode, decay, update, st, it, p, shmem, s);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+int launch_assign(const AssignParams &p, hipStream_t s) {
+    dl_assign_kernel<<<dim3(p.nunits), dim3(256), 0, s>>>(p);
+    return (int)hipGetLastError();
+}
+
+}  // namespace dl
+
+struct dl_pool {
+    dl_pool_desc desc;
+    dl_pool_buffers buf;
+    bool dry;                       // host-only pool: validate + mirror, no device work
+    std::vector<int32_t> n;         // host mirror of live-log length per slot
+    std::vector<uint32_t> seen;     // duplicate detection (generation stamps)
+    uint32_t gen;
+};
+
+namespace {
+
+int check_slots(dl_pool *pool, int32_t B, const int32_t *ids) {
+    if (B < 0) return fail(DL_ERR_INVALID_ARG, "negative count %d", B);
+    if (B > pool->desc.max_batch)
+        return fail(DL_ERR_BATCH_TOO_LARGE, "batch %d exceeds max_batch %d", B, pool->desc.max_batch);
+    if (B > 0 && !ids) return fail(DL_ERR_INVALID_ARG, "slot_ids is NULL");
+    if (++pool->gen == 0) {           // stamp wrapped: clear and restart
+        std::fill(pool->seen.begin(), pool->seen.end(), 0u);
+        pool->gen = 1;
+    }
+    for (int32_t j = 0; j < B; ++j) {
+        const int32_t s = ids[j];
+        if (s < 0 || s >= pool->desc.num_slots)
+            return fail(DL_ERR_SLOT_RANGE, "slot id %d at position %d outside [0, %d)", s, j, pool->desc.num_slots);
+        if (pool->seen[s] == pool->gen) return fail(DL_ERR_DUPLICATE_SLOT, "slot id %d repeated (position %d)", s, j);
+        pool->seen[s] = pool->gen;
+    }
+    return DL_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(DL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared by dl_decode_step and dl_eager_step.
+int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const void *a_or_k, const void *b_or_v,
+           const float *lambda, const float *beta, float *out, void *stream, bool eager_call) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    const dl_pool_desc &d = pool->desc;
+    if (eager_call && d.merge_interval != 1)
+        return fail(DL_ERR_INVALID_ARG, "dl_eager_step needs a pool with merge_interval == 1 (got %d)", d.merge_interval);
+    int rc = check_slots(pool, B, ids);
+    if (rc) return rc;
+    if (d.decay == DL_DECAY_NONE && lambda) return fail(DL_ERR_INVALID_ARG, "lambda must be NULL for DL_DECAY_NONE");
+    if (d.update == DL_UPDATE_PLAIN && beta) return fail(DL_ERR_INVALID_ARG, "beta must be NULL for DL_UPDATE_PLAIN");
+    if (B == 0) return ok();
+    if (!pool->dry) {
+        if (!q || !a_or_k || !b_or_v || !out) return fail(DL_ERR_INVALID_ARG, "NULL q / a_or_k / b_or_v / out");
+        if (d.decay != DL_DECAY_NONE && !lambda) return fail(DL_ERR_INVALID_ARG, "lambda is NULL");
+        if (d.update == DL_UPDATE_DELTA && !beta) return fail(DL_ERR_INVALID_ARG, "beta is NULL");
+        const uintptr_t align = (uintptr_t)q | (uintptr_t)a_or_k | (uintptr_t)b_or_v | (uintptr_t)out;
+        if (align & 15) return fail(DL_ERR_INVALID_ARG, "token buffers must be 16-byte aligned");
+
+        const int C = d.merge_interval - 1;
+        const int mode = C == 0 ? dl::MODE_EAGER : dl::MODE_STEP;
+        const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
+        const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
+        const size_t shmem = (size_t)C * D * sizeof(float);
+        dl::StepParams p;
+        memset(&p, 0, sizeof p);
+        p.base = pool->buf.base;
+        p.klog = pool->buf.klog;
+        p.ulog = pool->buf.ulog;
+        p.lamlog = pool->buf.lamlog;
+        p.nlog = pool->buf.nlog;
+        p.H_v = d.num_v_heads;
+        p.H_k = d.num_k_heads;
+        p.C = C;
+        for (int32_t lo = 0; lo < B; lo += dl::kMaxLaunchSlots) {
+            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, B - lo);
+            p.q = static_cast<const char *>(q) + (size_t)lo * Hk * D * s_in;
+            p.k = static_cast<const char *>(a_or_k) + (size_t)lo * Hk * D * s_in;
+            p.v = static_cast<const char *>(b_or_v) + (size_t)lo * Hv * D * s_in;
+            p.lam = lambda ? lambda + (size_t)lo * Hv * lam_w : nullptr;
+            p.beta = beta ? beta + (size_t)lo * Hv : nullptr;
+            p.out = out + (size_t)lo * Hv * D;
+            p.nunits = cnt * d.num_v_heads;
+            memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+            const int e = dl::launch_step(d.d_k, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p, shmem,
+                                          (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail((hipError_t)e, "decode kernel launch");
+        }
+    }
+    const int32_t C = d.merge_interval - 1;
+    for (int32_t j = 0; j < B; ++j) {
+        int32_t &n = pool->n[ids[j]];
+        n = (n == C) ? 0 : n + 1;
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dl_pool_sizes(const dl_pool_desc *desc, size_t bytes_out[DL_NUM_BUFS]) {
+    int rc = validate_desc(desc);
+    if (rc) return rc;
+    if (!bytes_out) return fail(DL_ERR_INVALID_ARG, "bytes_out is NULL");
+    compute_sizes(desc, bytes_out);
+    return ok();
+}
+
+int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_pool **out) {
+    int rc = validate_desc(desc);
+    if (rc) return rc;
+    if (!out) return fail(DL_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    size_t sz[DL_NUM_BUFS];
+    compute_sizes(desc, sz);
+    if (buffers) {
+        const void *ptrs[DL_NUM_BUFS] = {buffers->base, buffers->klog, buffers->ulog, buffers->lamlog, buffers->nlog};
+        for (int i = 0; i < DL_NUM_BUFS; ++i) {
+            if (sz[i] && !ptrs[i]) return fail(DL_ERR_INVALID_ARG, "buffer %d is NULL but needs %zu bytes", i, sz[i]);
+            if ((uintptr_t)ptrs[i] & 15) return fail(DL_ERR_INVALID_ARG, "buffer %d is not 16-byte aligned", i);
+        }
+    }
+    dl_pool *p = new (std::nothrow) dl_pool;
+    if (!p) return fail(DL_ERR_INVALID_ARG, "out of host memory");
+    p->desc = *desc;
+    p->dry = buffers == nullptr;
+    if (buffers) p->buf = *buffers;
+    else memset(&p->buf, 0, sizeof p->buf);
+    p->n.assign(desc->num_slots, 0);
+    p->seen.assign(desc->num_slots, 0u);
+    p->gen = 0;
+    if (!p->dry) {
+        const size_t cnt = sz[DL_BUF_NLOG] / 4;
+        const int blocks = (int)std::min<size_t>((cnt + 255) / 256, 4096);
+        dl_zero_i32_kernel<<<dim3(blocks), dim3(256), 0, 0>>>(p->buf.nlog, cnt);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamSynchronize(0);
+        if (e != hipSuccess) {
+            delete p;
+            return hip_fail(e, "clearing log lengths");
+        }
+    }
+    *out = p;
+    return ok();
+}
+
+int dl_pool_destroy(dl_pool *pool) {
+    delete pool;
+    return ok();
+}
+
+int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids, const void *init_base, void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_slots(pool, n, slot_ids);
+    if (rc) return rc;
+    if (init_base && ((uintptr_t)init_base & 15)) return fail(DL_ERR_INVALID_ARG, "init_base is not 16-byte aligned");
+    if (n == 0) return ok();
+    if (!pool->dry) {
+        const dl_pool_desc &d = pool->desc;
+        dl::AssignParams p;
+        memset(&p, 0, sizeof p);
+        p.base = pool->buf.base;
+        p.nlog = pool->buf.nlog;
+        p.head_bytes = (int64_t)d.d_k * d.d_v * dtype_size(d.state_dtype);
+        p.H_v = d.num_v_heads;
+        for (int32_t lo = 0; lo < n; lo += dl::kMaxLaunchSlots) {
+            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, n - lo);
+            p.init = init_base ? static_cast<const char *>(init_base) + (size_t)lo * d.num_v_heads * p.head_bytes
+                               : nullptr;
+            p.nunits = cnt * d.num_v_heads;
+            memcpy(p.slots, slot_ids + lo, cnt * sizeof(int32_t));
+            const int e = dl::launch_assign(p, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail((hipError_t)e, "assign kernel launch");
+        }
+    }
+    for (int32_t j = 0; j < n; ++j) pool->n[slot_ids[j]] = 0;
+    return ok();
+}
+
+int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void *q, const void *a_or_k,
+                   const void *b_or_v, const float *lambda, const float *beta, float *out, void *stream) {
+    return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, false);
+}
+
+int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void *q, const void *a_or_k,
+                  const void *b_or_v, const float *lambda, const float *beta, float *out, void *stream) {
+    return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, true);
+}
+
+int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_slots(pool, n, slot_ids);
+    if (rc) return rc;
+    const dl_pool_desc &d = pool->desc;
+    // only slots with a non-empty log have anything to materialize
+    std::vector<int32_t> live;
+    live.reserve(n);
+    for (int32_t j = 0; j < n; ++j)
+        if (pool->n[slot_ids[j]] > 0) live.push_back(slot_ids[j]);
+    if (!pool->dry && !live.empty()) {
+        const int C = d.merge_interval - 1;
+        dl::StepParams p;
+        memset(&p, 0, sizeof p);
+        p.base = pool->buf.base;
+        p.klog = pool->buf.klog;
+        p.ulog = pool->buf.ulog;
+        p.lamlog = pool->buf.lamlog;
+        p.nlog = pool->buf.nlog;
+        p.H_v = d.num_v_heads;
+        p.H_k = d.num_k_heads;
+        p.C = C;
+        const size_t shmem = (size_t)C * d.d_k * sizeof(float);
+        for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
+            const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);
+            p.nunits = cnt * d.num_v_heads;
+            memcpy(p.slots, live.data() + lo, cnt * sizeof(int32_t));
+            const int e = dl::launch_step(d.d_k, dl::MODE_MERGE, d.decay, d.update, d.state_dtype, d.in_dtype, p,
+                                          shmem, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail((hipError_t)e, "merge kernel launch");
+        }
+    }
+    for (int32_t s : live) pool->n[s] = 0;
+    return ok();
+}
+
+int dl_flush_all(dl_pool *pool, void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    std::vector<int32_t> live;
+    for (int32_t s = 0; s < pool->desc.num_slots; ++s)
+        if (pool->n[s] > 0) live.push_back(s);
+    for (size_t lo = 0; lo < live.size(); lo += pool->desc.max_batch) {
+        const int32_t cnt = (int32_t)std::min<size_t>(pool->desc.max_batch, live.size() - lo);
+        int rc = dl_merge(pool, cnt, live.data() + lo, stream);
+        if (rc) return rc;
+    }
+    return ok();
+}
+
+int dl_get_log_len(const dl_pool *pool, int32_t *n_out) {
+    if (!pool || !n_out) return fail(DL_ERR_INVALID_ARG, "NULL argument");
+    memcpy(n_out, pool->n.data(), pool->n.size() * sizeof(int32_t));
+    return ok();
+}
+
+int dl_schedule(const dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t *merge_out, int32_t *index_out) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    if (B > 0 && (!merge_out || !index_out)) return fail(DL_ERR_INVALID_ARG, "NULL output array");
+    int rc = check_slots(const_cast<dl_pool *>(pool), B, slot_ids);
+    if (rc) return rc;
+    const int32_t C = pool->desc.merge_interval - 1;
+    for (int32_t j = 0; j < B; ++j) {
+        const int32_t n = pool->n[slot_ids[j]];
+        merge_out[j] = n == C ? 1 : 0;
+        index_out[j] = n;
+    }
+    return ok();
+}
+
+int dl_read_log_len_device(dl_pool *pool, int32_t *n_out, void *stream) {
+    if (!pool || !n_out) return fail(DL_ERR_INVALID_ARG, "NULL argument");
+    if (pool->dry) return fail(DL_ERR_DRY_RUN, "host-only pool has no device counters");
+    const size_t bytes = (size_t)pool->desc.num_slots * pool->desc.num_v_heads * sizeof(int32_t);
+    hipError_t e = hipMemcpyAsync(n_out, pool->buf.nlog, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "reading log lengths");
+    return ok();
+}
+
+const char *dl_last_error(void) { return g_err.c_str(); }
+
+int32_t dl_launch_slot_limit(void) { return dl::kMaxLaunchSlots; }
+
+}  // extern "C"

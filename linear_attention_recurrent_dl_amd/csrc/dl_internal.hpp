@@ -1,0 +1,68 @@
+// Internal declarations shared by the host library and the kernel translation
+// units.  Not part of the public C ABI (that is include/deltalog.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dl {
+
+// Slot ids travel to the device inside the kernel argument block, so a launch
+// carries at most this many decoded slots; larger calls are split on the host.
+constexpr int kMaxLaunchSlots = 512;
+
+// Largest log capacity C = L - 1 (sizes the per-block coefficient arrays).
+constexpr int kMaxLogCap = 63;
+
+enum Mode : int {
+    MODE_STEP = 0,   // DeltaLog decode: append, or merge when the log is full
+    MODE_EAGER = 1,  // eager read-modify-write of the dense state (no log)
+    MODE_MERGE = 2,  // materialize base + log, no token
+};
+
+enum DType : int { F32 = 0, BF16 = 1 };
+enum Decay : int { DECAY_NONE = 0, DECAY_SCALAR = 1, DECAY_PER_KEY = 2 };
+
+// Arguments of the decode / eager / merge kernels.  Token-side pointers are
+// already offset to this launch's first batch entry.
+struct StepParams {
+    void *base;          // [P, H_v, D, D]       state dtype
+    void *klog;          // [P, H_k, C, D]       input dtype
+    void *ulog;          // [P, H_v, C, D]       fp32 (delta) | input dtype (plain)
+    float *lamlog;       // [P, H_v, C] | [P, H_v, C, D]
+    int32_t *nlog;       // [P, H_v]
+    const void *q;       // [n, H_k, D]
+    const void *k;       // [n, H_k, D]
+    const void *v;       // [n, H_v, D]
+    const float *lam;    // [n, H_v] | [n, H_v, D]
+    const float *beta;   // [n, H_v]
+    float *out;          // [n, H_v, D]
+    int32_t H_v;
+    int32_t H_k;
+    int32_t C;           // log capacity L - 1
+    int32_t nunits;      // blocks in this launch = n * H_v
+    int32_t slots[kMaxLaunchSlots];
+};
+
+// Arguments of the slot-assignment (fresh base, empty log) kernel.
+struct AssignParams {
+    void *base;          // [P, H_v, D, D]
+    int32_t *nlog;       // [P, H_v]
+    const void *init;    // [n, H_v, D, D] or NULL (zero state)
+    int64_t head_bytes;  // D * D * sizeof(state)
+    int32_t H_v;
+    int32_t nunits;      // n * H_v
+    int32_t slots[kMaxLaunchSlots];
+};
+
+// Threads per block of the decode kernels for a head dim and state dtype.
+int block_threads(int D, int state_dtype);
+
+// Launch one decode / eager / merge kernel; returns hipError_t as int.
+int launch_step(int D, int mode, int decay, int update, int state_dtype, int in_dtype,
+                const StepParams &p, size_t shmem, hipStream_t stream);
+
+int launch_assign(const AssignParams &p, hipStream_t stream);
+
+}  // namespace dl

@@ -1,0 +1,448 @@
+// DeltaLog decode-step kernels for CDNA4 (gfx950).
+//
+// Sources: [DL] "DeltaLog: Deferred Materialization of Recurrent States for
+// Linear Attention Decoding" -- Eq. 3, the append-merge cycle and logical-state
+// equation of the design section, and the GPU-execution section (ReplayPrep,
+// AppendDecode, Finalize, Merge); [FPGA] "A Persistent-State Dataflow
+// Accelerator for Memory-Bound Linear Attention Decode on FPGA" -- grouped
+// value heads.
+//
+// One block owns one (slot, v-head) pair and the whole d_k x d_v tile, so the
+// paper's ReplayPrep (key-side replay coefficients) and Finalize (commit the
+// log length once) fuse into the block with no scratch buffer and no second
+// launch.  Per block:
+//
+//   1. issue the base-tile loads: every thread holds RPT rows x VEC columns as
+//      16-byte vectors; for a fixed row index the block reads NT x 16
+//      contiguous bytes (fully coalesced, one pass over the base)
+//   2. l' = l_bar + lambda (l_bar = newest snapshot, or 0 for an empty log);
+//      q~ = e^{l'} * q and k~ = e^{l'} * k go to LDS
+//   3. replay coefficients per live entry i (one wave per entry, cross-lane
+//      sums): c^q_i = sum_r e^{l'_r - Lam_ir} K_ir q_r, c^k_i likewise with k,
+//      and the merge-time key factors e^{l' - Lam_i} * K_i into LDS
+//   4. y_q = S_bar^T q~ + sum_i c^q_i U_i and y_k = S_bar^T k~ + sum_i c^k_i U_i:
+//      per-thread FMAs over its rows, then xor-shuffles across the row groups
+//      of a wave and an LDS sum across waves
+//   5. per column: b = beta (v - y_k) (delta) or the given b; o = y_q + (a.q) b
+//   6. append: write U[n] <- b, K[n] <- a (the first v-head of a q/k group
+//      owns the shared key entry), Lam[n] <- l', n <- n + 1
+//      merge:  S_bar <- e^{l'} * S_bar + sum_i (e^{l'-Lam_i} K_i) U_i^T + a b^T
+//      from the tile still in registers, n <- 0
+//
+// The eager baseline is the same block with no log: always step 6's merge
+// branch with n = 0, i.e. read S, decay, correct, add the outer product, write
+// S.  The standalone merge uses the same code with no token (lambda = 0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "dl_internal.hpp"
+
+namespace dl {
+
+typedef uint16_t bf16_t;   // IEEE bfloat16 bit pattern
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+    // round to nearest, ties to even (finite inputs)
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// N consecutive elements of T starting at p (N * sizeof(T) in {4, 8, 16, 32}
+// bytes, p aligned to that size up to 16), widened to fp32.
+template <typename T, int N>
+__device__ __forceinline__ void load_f32(const T *__restrict__ p, float (&out)[N]) {
+    constexpr int BYTES = N * (int)sizeof(T);
+    static_assert(BYTES % 4 == 0, "vector of at least 4 bytes");
+    if constexpr (BYTES >= 16) {
+        const uint4 *v = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+        for (int c = 0; c < BYTES / 16; ++c) {
+            uint4 w = v[c];
+            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(T) == 4) {
+                    out[c * 4 + j] = __uint_as_float(ws[j]);
+                } else {
+                    out[c * 8 + 2 * j] = __uint_as_float(ws[j] << 16);
+                    out[c * 8 + 2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+                }
+            }
+        }
+    } else if constexpr (BYTES == 8) {
+        uint2 w = *reinterpret_cast<const uint2 *>(p);
+        uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (sizeof(T) == 4) {
+                out[j] = __uint_as_float(ws[j]);
+            } else {
+                out[2 * j] = __uint_as_float(ws[j] << 16);
+                out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+        if constexpr (sizeof(T) == 4) {
+            out[0] = __uint_as_float(w);
+        } else {
+            out[0] = __uint_as_float(w << 16);
+            out[1] = __uint_as_float(w & 0xFFFF0000u);
+        }
+    }
+}
+
+// Unpack a 16-byte register vector of T into fp32.
+template <typename T, int N>
+__device__ __forceinline__ void unpack_f32(const uint4 &w, float (&out)[N]) {
+    static_assert(N * sizeof(T) == 16, "one 16-byte vector");
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 4) {
+            out[j] = __uint_as_float(ws[j]);
+        } else {
+            out[2 * j] = __uint_as_float(ws[j] << 16);
+            out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <typename T, int N>
+__device__ __forceinline__ uint4 pack_16(const float (&x)[N]) {
+    static_assert(N * sizeof(T) == 16, "one 16-byte vector");
+    uint32_t ws[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 4) {
+            ws[j] = __float_as_uint(x[j]);
+        } else {
+            ws[j] = (uint32_t)from_f32<bf16_t>(x[2 * j]) | ((uint32_t)from_f32<bf16_t>(x[2 * j + 1]) << 16);
+        }
+    }
+    return make_uint4(ws[0], ws[1], ws[2], ws[3]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs.  Renumber them so that
+// each XCD works on a contiguous range of (entry, head) units: the v-heads of
+// one q/k group (which share the key-log entries and q/k) then meet in the
+// same L2.
+__device__ __forceinline__ int xcd_unit(int bid, int nb) {
+    if ((nb & 7) != 0) return bid;
+    return (bid & 7) * (nb >> 3) + (bid >> 3);
+}
+
+// Block geometry for a D x D tile of state type ST.
+template <int D, typename ST>
+struct Tile {
+    static constexpr int VEC = 16 / (int)sizeof(ST);       // elements per 16-byte load
+    static constexpr int CG = D / VEC;                     // column groups per row
+    static constexpr int NT = D >= 128 ? 256 : (D >= 64 ? 128 : 64);
+    static constexpr int RG = NT / CG;                     // row groups
+    static constexpr int RPT = (D + RG - 1) / RG;          // rows per thread
+    static constexpr int NW = NT / 64;                     // waves per block
+    static constexpr bool RAGGED = RG > D;                 // some row groups own no row
+    static_assert(D % VEC == 0 && NT % CG == 0 && CG <= 64, "tile geometry");
+};
+
+template <int D, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
+__global__ void __launch_bounds__((Tile<D, ST>::NT))
+dl_step_kernel(const StepParams p) {
+    using G = Tile<D, ST>;
+    using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
+    constexpr int VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    constexpr bool TOKEN = MODE != MODE_MERGE;
+    constexpr bool LOG = MODE != MODE_EAGER;
+
+    __shared__ float s_q[D];        // e^{l'} * q
+    __shared__ float s_k[D];        // e^{l'} * k
+    __shared__ float s_qr[D];       // q
+    __shared__ float s_a[D];        // a (= k for delta)
+    __shared__ float s_g[D];        // e^{l'}
+    __shared__ float s_lp[D];       // l'
+    __shared__ float s_b[D];        // b (merge broadcast)
+    __shared__ float s_cq[kMaxLogCap + 1];
+    __shared__ float s_ck[kMaxLogCap + 1];
+    __shared__ float s_red[NW][2][D];
+    __shared__ float s_s;           // a . q
+    extern __shared__ float s_kt[]; // [C][D] merge-time key factors e^{l'-Lam_i} * K_i
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int H_v = p.H_v, C = p.C;
+    const int e = unit / H_v, h = unit - e * H_v;
+    const int grp = H_v / p.H_k, g = h / grp;
+    const int slot = p.slots[e];
+    const size_t sh = (size_t)slot * H_v + h;           // slot-head index
+    const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
+    const int cg = tid % CG, rg = tid / CG;
+
+    int n = 0;
+    if constexpr (LOG) n = p.nlog[sh];
+    if constexpr (MODE == MODE_MERGE) {
+        if (n == 0) return;                             // empty log: nothing to materialize
+    }
+    const bool merge = (MODE != MODE_STEP) || (n == C);
+
+    // 1. base tile -> registers
+    const ST *base = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D);
+    uint4 tile[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = rg + RG * j;
+        if (!G::RAGGED || r < D) tile[j] = *reinterpret_cast<const uint4 *>(base + r * D + cg * VEC);
+        else tile[j] = make_uint4(0, 0, 0, 0);
+    }
+
+    const IT *klog = reinterpret_cast<const IT *>(p.klog);
+    const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
+    const float *lamlog = p.lamlog;
+
+    // 2. decay bookkeeping and decayed q, k
+    if (tid < D) {
+        float lbar = 0.f, lam = 0.f;
+        if constexpr (DECAY == DECAY_SCALAR) {
+            if (LOG && n > 0) lbar = lamlog[sh * C + (n - 1)];
+            if (TOKEN) lam = p.lam[(size_t)e * H_v + h];
+        } else if constexpr (DECAY == DECAY_PER_KEY) {
+            if (LOG && n > 0) lbar = lamlog[(sh * C + (n - 1)) * D + tid];
+            if (TOKEN) lam = p.lam[((size_t)e * H_v + h) * D + tid];
+        }
+        const float lp = lbar + lam;
+        const float gg = (DECAY == DECAY_NONE) ? 1.f : __expf(lp);
+        s_lp[tid] = lp;
+        s_g[tid] = gg;
+        if constexpr (TOKEN) {
+            const size_t qo = ((size_t)e * p.H_k + g) * D + tid;
+            const float qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+            const float kv = to_f32(reinterpret_cast<const IT *>(p.k)[qo]);
+            s_qr[tid] = qv;
+            s_a[tid] = kv;
+            s_q[tid] = gg * qv;
+            s_k[tid] = gg * kv;
+        }
+    }
+    __syncthreads();
+
+    // 3. replay coefficients (one wave per live entry) and a . q
+    for (int i = wave; i <= n; i += NW) {
+        if (i == n) {
+            if constexpr (TOKEN) {
+                float acc = 0.f;
+                for (int r = lane; r < D; r += 64) acc += s_a[r] * s_qr[r];
+                acc = wave_sum(acc);
+                if (lane == 0) s_s = acc;
+            }
+            continue;
+        }
+        const IT *Ki = klog + (gk * C + i) * D;
+        float wsc = 1.f;
+        if constexpr (DECAY == DECAY_SCALAR) wsc = __expf(s_lp[0] - lamlog[sh * C + i]);
+        float pq = 0.f, pk = 0.f;
+        for (int r = lane; r < D; r += 64) {
+            float w = wsc;
+            if constexpr (DECAY == DECAY_PER_KEY) w = __expf(s_lp[r] - lamlog[(sh * C + i) * D + r]);
+            const float kt = w * to_f32(Ki[r]);
+            if (merge) s_kt[i * D + r] = kt;
+            if constexpr (TOKEN) {
+                pq += kt * s_qr[r];
+                if constexpr (DELTA) pk += kt * s_a[r];
+            }
+        }
+        if constexpr (TOKEN) {
+            pq = wave_sum(pq);
+            if constexpr (DELTA) pk = wave_sum(pk);
+            if (lane == 0) {
+                s_cq[i] = pq;
+                s_ck[i] = pk;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 4-6. projections, value factor, output, append commit
+    if constexpr (TOKEN) {
+        float accq[VEC], acck[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) accq[c] = acck[c] = 0.f;
+        if constexpr (LOG) {
+            for (int i = rg; i < n; i += RG) {             // log entries as extra rows
+                float u[VEC];
+                load_f32<BT, VEC>(ulog + (sh * C + i) * D + cg * VEC, u);
+                const float cq = s_cq[i], ck = s_ck[i];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+                    accq[c] += cq * u[c];
+                    if constexpr (DELTA) acck[c] += ck * u[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const int r = rg + RG * j;
+            if (!G::RAGGED || r < D) {
+                float x[VEC];
+                unpack_f32<ST, VEC>(tile[j], x);
+                const float qr = s_q[r];
+                const float kr = DELTA ? s_k[r] : 0.f;
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) {
+                    accq[c] += x[c] * qr;
+                    if constexpr (DELTA) acck[c] += x[c] * kr;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                accq[c] += __shfl_xor(accq[c], off, 64);
+                if constexpr (DELTA) acck[c] += __shfl_xor(acck[c], off, 64);
+            }
+        }
+        if (lane < CG) {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                s_red[wave][0][cg * VEC + c] = accq[c];
+                s_red[wave][1][cg * VEC + c] = acck[c];
+            }
+        }
+        __syncthreads();
+
+        if (tid < D) {
+            float yq = 0.f, yk = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                yq += s_red[w][0][tid];
+                yk += s_red[w][1][tid];
+            }
+            const size_t vo = ((size_t)e * H_v + h) * D + tid;
+            const float vin = to_f32(reinterpret_cast<const IT *>(p.v)[vo]);
+            float b;
+            if constexpr (DELTA) b = p.beta[(size_t)e * H_v + h] * (vin - yk);
+            else b = vin;
+            p.out[vo] = yq + s_s * b;
+            if (merge) {
+                s_b[tid] = b;
+            } else if constexpr (LOG) {
+                BT *ulw = reinterpret_cast<BT *>(p.ulog);
+                ulw[(sh * C + n) * D + tid] = from_f32<BT>(b);
+                if (h % grp == 0) {                        // designated writer of the key entry
+                    IT *klw = reinterpret_cast<IT *>(p.klog);
+                    klw[(gk * C + n) * D + tid] = reinterpret_cast<const IT *>(p.k)[((size_t)e * p.H_k + g) * D + tid];
+                }
+                if constexpr (DECAY == DECAY_PER_KEY) p.lamlog[(sh * C + n) * D + tid] = s_lp[tid];
+                if constexpr (DECAY == DECAY_SCALAR) {
+                    if (tid == 0) p.lamlog[sh * C + n] = s_lp[0];
+                }
+            }
+        }
+    }
+    if constexpr (LOG) {
+        if (tid == 0) p.nlog[sh] = merge ? 0 : n + 1;
+    }
+    if (!merge) return;
+
+    // merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T, from registers
+    __syncthreads();
+    float acc[RPT][VEC];
+    float bcol[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) bcol[c] = TOKEN ? s_b[cg * VEC + c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = rg + RG * j;
+        const int rr = r < D ? r : 0;
+        unpack_f32<ST, VEC>(tile[j], acc[j]);
+        const float gr = s_g[rr];
+        const float ar = TOKEN ? s_a[rr] : 0.f;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[j][c] = gr * acc[j][c] + ar * bcol[c];
+    }
+    if constexpr (LOG) {
+        for (int i = 0; i < n; ++i) {
+            float u[VEC];
+            load_f32<BT, VEC>(ulog + (sh * C + i) * D + cg * VEC, u);
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const int r = rg + RG * j;
+                const float kt = s_kt[i * D + (r < D ? r : 0)];
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[j][c] += kt * u[c];
+            }
+        }
+    }
+    ST *basew = reinterpret_cast<ST *>(p.base) + sh * (size_t)(D * D);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int r = rg + RG * j;
+        if (!G::RAGGED || r < D) *reinterpret_cast<uint4 *>(basew + r * D + cg * VEC) = pack_16<ST, VEC>(acc[j]);
+    }
+}
+
+template <int D, int DECAY, bool DELTA, typename ST, typename IT>
+static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipStream_t s) {
+    constexpr int NT = Tile<D, ST>::NT;
+    const dim3 grid(p.nunits), block(NT);
+    switch (mode) {
+    case MODE_STEP:
+        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p);
+        break;
+    case MODE_EAGER:
+        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p);
+        break;
+    case MODE_MERGE:
+        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D, int DECAY, bool DELTA>
+static hipError_t launch_dtypes(int mode, int st, int it, const StepParams &p, size_t shmem, hipStream_t s) {
+    if (st == F32 && it == F32) return launch_combo<D, DECAY, DELTA, float, float>(mode, p, shmem, s);
+    if (st == F32 && it == BF16) return launch_combo<D, DECAY, DELTA, float, bf16_t>(mode, p, shmem, s);
+    if (st == BF16 && it == F32) return launch_combo<D, DECAY, DELTA, bf16_t, float>(mode, p, shmem, s);
+    if (st == BF16 && it == BF16) return launch_combo<D, DECAY, DELTA, bf16_t, bf16_t>(mode, p, shmem, s);
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_step_d(int mode, int decay, int update, int st, int it, const StepParams &p,
+                         size_t shmem, hipStream_t s) {
+    const bool delta = update != 0;
+    switch (decay) {
+    case DECAY_NONE:
+        return delta ? launch_dtypes<D, DECAY_NONE, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, DECAY_NONE, false>(mode, st, it, p, shmem, s);
+    case DECAY_SCALAR:
+        return delta ? launch_dtypes<D, DECAY_SCALAR, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, DECAY_SCALAR, false>(mode, st, it, p, shmem, s);
+    case DECAY_PER_KEY:
+        return delta ? launch_dtypes<D, DECAY_PER_KEY, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, DECAY_PER_KEY, false>(mode, st, it, p, shmem, s);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dl

@@ -1,0 +1,199 @@
+"""The C ABI on the host: exports, sizing, validation, and the append/merge
+bookkeeping of a host-only pool against the oracle's closed-form schedule.
+
+No compute call runs here (a host-only pool enqueues nothing)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_recurrent_dl_amd as dl
+from linear_attention_recurrent_dl_amd import _native as N
+from oracle import schedule
+from workloads import CONFIGS, Workload, small_variant
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltalog.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|const char \*)\s*(dl_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.lib()
+    names = header_functions()
+    assert len(names) >= 13, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in deltalog.h but not exported"
+    assert set(names) == set(N.EXPORTED)
+
+
+def test_binding_names_match_c_names():
+    for name in header_functions():
+        assert callable(getattr(dl, name)), name
+
+
+def _desc(**kw):
+    base = dict(num_slots=8, max_batch=4, H_v=4, H_k=2, d=64, L=8, decay="per_key",
+                update="delta", state_dtype="f32", in_dtype="bf16")
+    base.update(kw)
+    return dl.make_desc(**base)
+
+
+def test_pool_sizes_formula():
+    for cfg in CONFIGS.values():
+        desc = dl.make_desc(cfg.num_slots, cfg.batch, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay,
+                            cfg.update, cfg.state_dtype, cfg.in_dtype)
+        sz = dl.dl_pool_sizes(desc)
+        P, Hv, Hk, D, C = cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, cfg.L - 1
+        s_st = 2 if cfg.state_dtype == "bf16" else 4
+        s_in = 2 if cfg.in_dtype == "bf16" else 4
+        s_b = 4 if cfg.update == "delta" else s_in
+        lam_w = {"none": 0, "scalar": 1, "per_key": D}[cfg.decay]
+        assert sz == [P * Hv * D * D * s_st, P * Hk * C * D * s_in, P * Hv * C * D * s_b,
+                      P * Hv * C * lam_w * 4, P * Hv * 4], cfg.name
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_slots", 0, N.DL_ERR_INVALID_ARG),
+    ("max_batch", 0, N.DL_ERR_INVALID_ARG),
+    ("num_v_heads", 3, N.DL_ERR_INVALID_ARG),       # not a multiple of H_k = 2
+    ("num_k_heads", 0, N.DL_ERR_INVALID_ARG),
+    ("merge_interval", 0, N.DL_ERR_INVALID_ARG),
+    ("merge_interval", 65, N.DL_ERR_INVALID_ARG),
+    ("decay", 7, N.DL_ERR_INVALID_ARG),
+    ("update", 2, N.DL_ERR_INVALID_ARG),
+    ("state_dtype", 5, N.DL_ERR_INVALID_ARG),
+    ("d_k", 48, N.DL_ERR_UNSUPPORTED),
+    ("d_v", 32, N.DL_ERR_UNSUPPORTED),                # d_k != d_v
+])
+def test_descriptor_validation(field, value, code):
+    desc = _desc()
+    setattr(desc, field, value)
+    if field == "d_k":
+        desc.d_v = value
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_pool_sizes(desc)
+    assert ei.value.code == code
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_pool_create(desc, None)
+
+
+def test_create_rejects_missing_or_misaligned_buffers():
+    desc = _desc()
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_pool_create(desc, N.dl_pool_buffers(None, None, None, None, None))
+    assert ei.value.code == N.DL_ERR_INVALID_ARG
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_pool_create(desc, N.dl_pool_buffers(16, 32, 48, 64, 72))   # 72 not 16-aligned
+
+
+def _host_pool(**kw):
+    d = dict(num_slots=8, H_v=4, H_k=2, d=64, L=8, decay="per_key", update="delta",
+             state_dtype="f32", in_dtype="bf16", max_batch=4, device=None)
+    d.update(kw)
+    return dl.DeltaLogPool(**d)
+
+
+def test_errors_leave_pool_unchanged():
+    p = _host_pool()
+    p.decode_step([0, 1, 2])
+    before = p.log_len().copy()
+    cases = [([1, 1], N.DL_ERR_DUPLICATE_SLOT), ([0, 8], N.DL_ERR_SLOT_RANGE),
+             ([-1], N.DL_ERR_SLOT_RANGE), ([0, 1, 2, 3, 4], N.DL_ERR_BATCH_TOO_LARGE)]
+    for ids, code in cases:
+        for call in (p.decode_step, p.merge, p.assign):
+            with pytest.raises(dl.DeltaLogError) as ei:
+                call(ids)
+            assert ei.value.code == code, (ids, call)
+            assert np.array_equal(p.log_len(), before)
+    with pytest.raises(dl.DeltaLogError) as ei:
+        p.schedule([3, 3])
+    assert ei.value.code == N.DL_ERR_DUPLICATE_SLOT
+
+
+def test_token_pointer_rules():
+    lib = N.lib()
+    ids = np.array([0], dtype=np.int32)
+    ip = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p_none = _host_pool(decay="none", update="plain")
+    # lambda must be NULL without decay; beta NULL for plain
+    assert lib.dl_decode_step(p_none.handle, 1, ip, None, None, None, 16, None, None, None) == N.DL_ERR_INVALID_ARG
+    assert lib.dl_decode_step(p_none.handle, 1, ip, None, None, None, None, 16, None, None) == N.DL_ERR_INVALID_ARG
+    assert p_none.log_len().tolist() == [0] * 8
+    # eager step needs L == 1
+    p = _host_pool()
+    with pytest.raises(dl.DeltaLogError):
+        p.eager_step([0])
+    pe = _host_pool(L=1)
+    pe.eager_step([0, 1])
+    assert pe.log_len().tolist() == [0] * 8
+    # zero-length calls are no-ops
+    p.decode_step([])
+    p.merge([])
+    p.assign([])
+    assert p.log_len().tolist() == [0] * 8
+    with pytest.raises(dl.DeltaLogError) as ei:
+        p.device_log_len()
+    assert ei.value.code == N.DL_ERR_DRY_RUN
+
+
+@pytest.mark.parametrize("L", [1, 2, 5, 16])
+def test_host_schedule_matches_closed_form(L):
+    rng = np.random.default_rng(L)
+    P = 12
+    p = _host_pool(num_slots=P, L=L, max_batch=P)
+    cnt = schedule.Counters(P, L)
+    for t in range(80):
+        if t % 9 == 4:
+            rs = rng.choice(P, size=3, replace=False)
+            p.assign(rs)
+            cnt.reset(rs)
+        if t % 13 == 6:
+            ms = rng.choice(P, size=4, replace=False)
+            p.merge(ms)
+            cnt.merge(ms)
+        if t % 29 == 28:
+            p.flush_all()
+            cnt.merge(np.arange(P))
+        B = int(rng.integers(0, P + 1))
+        ids = rng.choice(P, size=B, replace=False)
+        merge, index = p.schedule(ids)
+        want = cnt.decode(ids)
+        assert merge.tolist() == [int(ph == schedule.MERGE) for ph, _ in want]
+        assert index.tolist() == [ix for _, ix in want]
+        p.decode_step(ids)
+        assert np.array_equal(p.log_len(), cnt.n)
+
+
+def test_host_schedule_serving_pool_workload():
+    """The serving-pool workload's bookkeeping (ragged fill, 51 replacements and
+    256 random slots per step) on a host-only pool, step by step."""
+    cfg = small_variant(CONFIGS[5], steps=64)
+    wl = Workload(cfg)
+    p = dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update,
+                        cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch, device=None)
+    cnt = schedule.Counters(cfg.num_slots, cfg.L)
+    for desc in wl.plan():
+        inp = wl.step_inputs(desc)
+        if len(inp.replace_ids):
+            p.assign(inp.replace_ids)
+            cnt.reset(inp.replace_ids)
+        merge, index = p.schedule(inp.slot_ids)
+        want = cnt.decode(inp.slot_ids)
+        assert merge.tolist() == [int(ph == schedule.MERGE) for ph, _ in want]
+        assert index.tolist() == [ix for _, ix in want]
+        p.decode_step(inp.slot_ids)
+        assert np.array_equal(p.log_len(), cnt.n)
+    # after the fill phase every slot had its drawn initial fill
+    wl2 = Workload(cfg)
+    cnt2 = schedule.Counters(cfg.num_slots, cfg.L)
+    for desc in wl2.fill_steps():
+        cnt2.decode(desc.slots)
+    assert np.array_equal(cnt2.n, wl2.initial_fill())

@@ -1,0 +1,125 @@
+"""HIP path vs the fp64 oracle (E, the eager recurrence), through the C ABI.
+
+Bar: outputs of every compared entry and final states rel-L2 <= 1e-4 (fp32
+state) or 2e-2 (bf16 state); schedule, live-log counters (device and host) and
+the lossless key-factor copies exact.
+"""
+
+import numpy as np
+import pytest
+
+from workloads import CONFIGS, headline_gdn, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(cfg, res):
+    from gpu_harness import tolerance
+    tol = tolerance(cfg)
+    assert res.sched_mismatch == 0
+    assert res.counter_mismatch == 0
+    assert res.klog_mismatch == 0
+    assert res.out_err <= tol, f"output rel-L2 {res.out_err:.3e} > {tol}"
+    assert res.state_err <= tol, f"state rel-L2 {res.state_err:.3e} > {tol}"
+
+
+# ---- the first two workloads at full size, every output compared
+@pytest.mark.parametrize("idx", [1, 2])
+def test_full_config(idx):
+    from gpu_harness import run
+    cfg = CONFIGS[idx]
+    res = run(cfg)
+    _check(cfg, res)
+    assert res.merges == cfg.steps // cfg.L * cfg.batch
+
+
+# ---- larger workloads at oracle-friendly sizes, every output compared
+SMALL = {
+    3: dict(batch=5, steps=96),
+    4: dict(batch=7, steps=48),
+    5: dict(num_slots=40, batch=13, steps=64, replace_per_step=2),
+}
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_small_config(idx):
+    from gpu_harness import run
+    cfg = small_variant(CONFIGS[idx], **SMALL[idx])
+    _check(cfg, run(cfg))
+
+
+# ---- full-size workloads in the launch configuration the benchmark times,
+#      compared on a sample of slots followed by the oracle
+TRACK = {3: [0, 31, 63], 4: [0, 77, 127], 5: [3, 100, 511, 777, 1023]}
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_full_size_sampled(idx):
+    from gpu_harness import run
+    cfg = CONFIGS[idx]
+    steps = None if idx != 5 else 256
+    _check(cfg, run(cfg, track=TRACK[idx], steps=steps))
+
+
+def test_headline_gdn_batch64_sampled():
+    from gpu_harness import run
+    cfg = headline_gdn(64, steps=64)
+    _check(cfg, run(cfg, track=[0, 63]))
+
+
+# ---- eager read-modify-write baseline kernel against the same oracle
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_eager_kernel(idx):
+    from gpu_harness import run
+    base = CONFIGS[idx]
+    cfg = base if idx <= 2 else small_variant(base, **SMALL[idx])
+    _check(cfg, run(cfg, eager=True))
+
+
+# ---- every operator / dtype combination on small tiles (incl. the d = 16
+#      bf16 tile whose row groups outnumber its rows), several merge intervals
+COMBOS = [(decay, update, st, it)
+          for decay in ("none", "scalar", "per_key")
+          for update in ("plain", "delta")
+          for st in ("f32", "bf16")
+          for it in ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(c))
+def test_operator_dtype_matrix(d, combo):
+    from gpu_harness import run
+    decay, update, st, it = combo
+    cfg = small_variant(CONFIGS[4], batch=3, steps=23, L=5, d=d, H_v=4, H_k=2, decay=decay,
+                        update=update, state_dtype=st, in_dtype=it,
+                        name=f"matrix_d{d}_{decay}_{update}_{st}_{it}",
+                        qk_dist="unit" if update == "delta" else "normal_scaled",
+                        qk_scale=0.25, v_scale=1.0 if update == "delta" else 0.25,
+                        lam_mu=None if decay == "none" else 3.0,
+                        lam_sigma=None if decay == "none" else 1.0,
+                        beta=update == "delta", init_sigma=0.02)
+    _check(cfg, run(cfg))
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 32, 64])
+def test_merge_intervals(L):
+    from gpu_harness import run
+    cfg = small_variant(CONFIGS[4], batch=4, steps=2 * L + 3, L=L, d=64, H_v=4, H_k=4,
+                        name=f"kda_L{L}")
+    _check(cfg, run(cfg))
+
+
+def test_explicit_merges_mid_stream():
+    from gpu_harness import run
+    cfg = small_variant(CONFIGS[2], steps=40, H_v=4, H_k=2, name="gdn_merge_every")
+    _check(cfg, run(cfg, merge_every=3))
+
+
+def test_batch_split_across_launches():
+    """More decoded slots than one launch carries: the host splits the batch."""
+    from gpu_harness import run
+    import linear_attention_recurrent_dl_amd as dl
+    lim = dl.dl_launch_slot_limit()
+    cfg = small_variant(CONFIGS[1], batch=lim + 37, steps=10, L=4, d=16, H_v=2, H_k=1,
+                        name="split_launch")
+    _check(cfg, run(cfg, track=[0, lim - 1, lim, lim + 36]))
