@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""DeltaLog decode-step benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--no-extra] [--no-cpu]
+
+A step is one decode of the workload's batch (for the serving pool: its fresh
+slot assignments, then the decode).  The headline workload is the 32-v-head
+d = 128 GDN decode at batch 1 (fp32 state, merge interval 16).  Inputs are the
+seeded synthetic ones from ``workloads`` and sit in device memory before the
+timed region; W untimed steps precede exactly K timed ones, bracketed by
+device synchronization.  Prints one JSON line.
+
+``roofline`` describes the decode kernel: algorithmic bytes per launch (the
+traffic model in ``linear_attention_recurrent_dl_amd.traffic`` summed over the
+entries of each launch with their actual live-log lengths) divided by the
+average launch duration, measured with HIP events recorded on the stream the
+kernel runs on.  ``workloads`` repeats the measurement for the batch >= 64
+workloads and the eager baseline; there, several independent pools (layers)
+are decoded in rotation so that the working set exceeds the 256 MB Infinity
+Cache and the bytes come from HBM.  ``cpu_baseline`` times the fp64 oracle on
+the host on a bounded sample of the headline workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "linear_attention_recurrent_dl_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", type=int, default=2, help="headline workload index (1-5)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
+    ap.add_argument("--extra", default="3,4,5,g64,g128,g256,g512",
+                    help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
+    ap.add_argument("--extra-steps", type=int, default=0, help="timed steps per extra workload (0 = 4 cycles)")
+    ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline runs")
+    ap.add_argument("--rotate-bytes", type=float, default=1.25 * 2 ** 30,
+                    help="minimum bytes of pools rotated per extra workload (cold cache)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--distinct-steps", type=int, default=0,
+                    help="distinct input steps staged per workload (0 = min(steps, 4 cycles))")
+    return ap.parse_args(argv)
+
+
+# --------------------------------------------------------------------------
+class Staged:
+    """A workload's pools and device-resident step inputs, ready to launch."""
+
+    def __init__(self, cfg, eager: bool, rotate: int, distinct: int, torch, dl, native):
+        from workloads import Workload
+        from linear_attention_recurrent_dl_amd import traffic
+
+        self.cfg, self.eager, self.R = cfg, eager, rotate
+        self.torch, self.N = torch, native
+        self.lib = native.lib()
+        wl = Workload(cfg)
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+        st, it = tdt[cfg.state_dtype], tdt[cfg.in_dtype]
+        L = 1 if eager else cfg.L
+        self.L = L
+        self.shape = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update,
+                                       cfg.state_dtype, cfg.in_dtype, L)
+        self.pools = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
+                                      cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch)
+                      for _ in range(rotate)]
+        self.shadow = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
+                                       cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch, device=None)
+                       for _ in range(rotate)]
+        # initial states: every slot's seeded base, copied to all rotated pools
+        for lo in range(0, cfg.num_slots, cfg.batch):
+            ids = np.arange(lo, min(cfg.num_slots, lo + cfg.batch), dtype=np.int32)
+            init = torch.from_numpy(wl.init_base(ids)).to("cuda").to(st).contiguous()
+            for p, sp in zip(self.pools, self.shadow):
+                p.assign(ids, init)
+                sp.assign(ids)
+            del init
+        self.bank = None
+        if cfg.replace_per_step:
+            self.bank = torch.from_numpy(wl.bank_states()).to("cuda").to(st).contiguous()
+        # ragged initial fill (serving pool): decode the fill steps, untimed
+        fill = wl.fill_steps()
+        for inp in wl.generate(fill):
+            self._decode_inputs_now(inp, it)
+        descs = wl.main_steps(distinct)
+        self.inputs = []
+        for inp in wl.generate(descs):
+            d = {"ids": np.ascontiguousarray(inp.slot_ids, dtype=np.int32),
+                 "q": torch.from_numpy(inp.q).to("cuda").to(it).contiguous(),
+                 "k": torch.from_numpy(inp.k).to("cuda").to(it).contiguous(),
+                 "v": torch.from_numpy(inp.v).to("cuda").to(it).contiguous(),
+                 "lam": None if inp.lam is None else torch.from_numpy(inp.lam).to("cuda"),
+                 "beta": None if inp.beta is None else torch.from_numpy(inp.beta).to("cuda"),
+                 "out": torch.empty((inp.batch, cfg.H_v, cfg.d), dtype=torch.float32, device="cuda"),
+                 "rep": np.ascontiguousarray(inp.replace_ids, dtype=np.int32),
+                 "rep_src": None}
+            if len(inp.replace_ids):
+                # bank entries are contiguous: the fresh states start at this offset
+                d["rep_src"] = self.bank[int(inp.replace_bank[0]):].data_ptr()
+            d["args"] = self._args(d)
+            self.inputs.append(d)
+        torch.cuda.synchronize()
+
+    def _decode_inputs_now(self, inp, it):
+        torch = self.torch
+        q = torch.from_numpy(inp.q).to("cuda").to(it).contiguous()
+        k = torch.from_numpy(inp.k).to("cuda").to(it).contiguous()
+        v = torch.from_numpy(inp.v).to("cuda").to(it).contiguous()
+        lam = None if inp.lam is None else torch.from_numpy(inp.lam).to("cuda")
+        beta = None if inp.beta is None else torch.from_numpy(inp.beta).to("cuda")
+        for p, sp in zip(self.pools, self.shadow):
+            if self.eager:
+                p.eager_step(inp.slot_ids, q, k, v, lam, beta)
+            else:
+                p.decode_step(inp.slot_ids, q, k, v, lam, beta)
+            sp.decode_step(inp.slot_ids)
+
+    def _args(self, d):
+        ids = d["ids"]
+        return (len(ids), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), d["q"].data_ptr(),
+                d["k"].data_ptr(), d["v"].data_ptr(),
+                None if d["lam"] is None else d["lam"].data_ptr(),
+                None if d["beta"] is None else d["beta"].data_ptr(), d["out"].data_ptr())
+
+    def plan_bytes(self, t0: int, count: int):
+        """Algorithmic decode bytes of steps t0 .. t0+count-1, from the host-only
+        shadow pools (same call sequence, nothing launched)."""
+        from linear_attention_recurrent_dl_amd import traffic
+        total = 0.0
+        assign_total = 0.0
+        for t in range(t0, t0 + count):
+            d = self.inputs[t % len(self.inputs)]
+            sp = self.shadow[t % self.R]
+            if len(d["rep"]):
+                sp.assign(d["rep"])
+                assign_total += len(d["rep"]) * self.cfg.H_v * traffic.assign_head_bytes(self.shape)
+            if self.eager:
+                total += len(d["ids"]) * self.cfg.H_v * traffic.eager_head_step_bytes(self.shape)
+            else:
+                _, idx = sp.schedule(d["ids"])
+                total += self.cfg.H_v * sum(traffic.deltalog_head_step_bytes(self.shape, int(n)) for n in idx)
+            sp.decode_step(d["ids"])
+        return total, assign_total
+
+    def run(self, t0: int, count: int, events=None):
+        """Launch steps t0 .. t0+count-1 on the current stream."""
+        torch = self.torch
+        stream = torch.cuda.current_stream().cuda_stream
+        dec = self.lib.dl_eager_step if self.eager else self.lib.dl_decode_step
+        asg = self.lib.dl_slot_assign
+        for t in range(t0, t0 + count):
+            d = self.inputs[t % len(self.inputs)]
+            pool = self.pools[t % self.R]
+            if len(d["rep"]):
+                rc = asg(pool.handle, len(d["rep"]), d["rep"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         d["rep_src"], stream)
+                if rc:
+                    self.N.check(rc, "dl_slot_assign")
+            if events is not None:
+                events[t - t0][0].record()
+            rc = dec(pool.handle, *d["args"], stream)
+            if rc:
+                self.N.check(rc, "decode")
+            if events is not None:
+                events[t - t0][1].record()
+
+    def close(self):
+        for p in self.pools:
+            p.close()
+        self.pools = []
+        self.inputs = []
+        self.bank = None
+
+
+def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native):
+    st = Staged(cfg, eager, rotate, distinct, torch, dl, native)
+    try:
+        st.plan_bytes(0, warmup)                 # advance the shadow schedule past warm-up
+        st.run(0, warmup)
+        torch.cuda.synchronize()
+        dec_bytes, asg_bytes = st.plan_bytes(warmup, steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t_start.record()
+        st.run(warmup, steps, ev)
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        total_ms = t_start.elapsed_time(t_end)
+        launch_ms = [a.elapsed_time(b) for a, b in ev]
+        return dict(total_ms=total_ms, wall_s=wall, launch_ms=launch_ms, dec_bytes=dec_bytes,
+                    asg_bytes=asg_bytes, L=st.L)
+    finally:
+        st.close()
+        torch.cuda.empty_cache()
+
+
+def summarize(cfg, r, steps, tag):
+    from linear_attention_recurrent_dl_amd import traffic
+    ms_step = r["total_ms"] / steps
+    head_steps = cfg.batch * cfg.H_v * steps
+    avg_launch_ms = float(np.mean(r["launch_ms"]))
+    med_launch_ms = float(np.median(r["launch_ms"]))
+    bytes_per_launch = r["dec_bytes"] / steps
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, r["L"])
+    return {
+        "workload": cfg.name, "kernel": tag, "batch": cfg.batch, "H_v": cfg.H_v, "H_k": cfg.H_k,
+        "d": cfg.d, "L": r["L"], "state": cfg.state_dtype,
+        "ms_per_step": ms_step,
+        "head_steps_per_s": head_steps / (r["total_ms"] * 1e-3),
+        "tokens_per_s": cfg.batch * steps / (r["total_ms"] * 1e-3),
+        "decode_launch_us_avg": avg_launch_ms * 1e3, "decode_launch_us_median": med_launch_ms * 1e3,
+        "decode_bytes_per_launch": bytes_per_launch,
+        "decode_GBps": achieved, "decode_frac_of_8TBps": achieved / PEAK_HBM_GBS,
+        "model_bytes_per_head_step": (traffic.eager_head_step_bytes(sh) if tag == "eager"
+                                      else traffic.deltalog_model_bytes(sh)),
+        "assign_bytes_per_step": r["asg_bytes"] / steps,
+    }
+
+
+def cpu_baseline(cfg, seconds: float):
+    """fp64 oracle (eager recurrence) on a bounded sample of the workload."""
+    import oracle
+    from workloads import Workload
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    wl = Workload(cfg)
+    ids = np.arange(cfg.num_slots, dtype=np.int32)
+    E = oracle.EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    inputs = wl.generate(wl.main_steps(min(cfg.steps, 64)))
+    E.step(inputs[0].slot_ids, inputs[0].q, inputs[0].k, inputs[0].v, inputs[0].lam, inputs[0].beta)
+    n, w0, c0 = 0, time.perf_counter(), time.process_time()
+    while True:
+        inp = inputs[(n + 1) % len(inputs)]
+        E.step(inp.slot_ids, inp.q, inp.k, inp.v, inp.lam, inp.beta)
+        n += 1
+        el = time.perf_counter() - w0
+        if (el >= seconds and n >= 32) or el >= 3 * seconds:
+            break
+    wall = time.perf_counter() - w0
+    cpu = time.process_time() - c0
+    return {"value": cfg.batch * cfg.H_v * n / wall, "unit": "head-steps/s",
+            "cores": max(1, int(round(cpu / wall))), "kind": "oracle",
+            "sample": f"{n} steps of {cfg.name} (all {cfg.batch * cfg.H_v} slot-heads each), fp64 NumPy "
+                      f"eager recurrence, {wall:.1f} s wall",
+            "tokens_per_s": cfg.batch * n / wall, "cpu_seconds": cpu, "blas_threads": blas_threads,
+            "host_cpus": os.cpu_count()}
+
+
+def extra_cfg(tag: str):
+    from workloads import CONFIGS, headline_gdn
+    if tag.startswith("g"):
+        return headline_gdn(int(tag[1:]))
+    return CONFIGS[int(tag)]
+
+
+def main(argv=None) -> int:
+    a = parse(argv)
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "requested_gpus": a.gpus}))
+        print("bench.py: only --gpus 1 is supported (one GPU per process, no multi-GPU path)",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from linear_attention_recurrent_dl_amd import _native as native
+    from workloads import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    native.lib()
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[a.workload]
+    steps, warmup = a.steps, a.warmup
+    distinct = a.distinct_steps or min(steps + warmup, 4 * cfg.L)
+    print(f"[bench] headline {cfg.describe()} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+
+    if a.calib_copy_mib:
+        src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    r = time_workload(cfg, False, steps, warmup, 1, distinct, torch, dl, native)
+    head = summarize(cfg, r, steps, "deltalog")
+    print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
+    eager_head = None
+    if not a.no_eager:
+        re_ = time_workload(cfg, True, steps, warmup, 1, min(distinct, 64), torch, dl, native)
+        eager_head = summarize(cfg, re_, steps, "eager")
+        print(f"[bench] {json.dumps(eager_head)}", file=sys.stderr, flush=True)
+
+    extras = []
+    if not a.no_extra:
+        for tag in [t for t in a.extra.split(",") if t]:
+            c = extra_cfg(tag)
+            from linear_attention_recurrent_dl_amd import traffic
+            ws = sum(dl.dl_pool_sizes(dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, c.L, c.decay,
+                                                   c.update, c.state_dtype, c.in_dtype)))
+            R = max(1, int(np.ceil(a.rotate_bytes / ws)))
+            xs = a.extra_steps or 4 * c.L
+            for eager in ([False] if a.no_eager else [False, True]):
+                rr = time_workload(c, eager, xs, c.L, R, min(4 * c.L, xs + c.L), torch, dl, native)
+                s = summarize(c, rr, xs, "eager" if eager else "deltalog")
+                s["rotated_pools"] = R
+                s["pool_bytes"] = ws if not eager else sum(dl.dl_pool_sizes(dl.make_desc(
+                    c.num_slots, c.batch, c.H_v, c.H_k, c.d, 1, c.decay, c.update, c.state_dtype, c.in_dtype)))
+                extras.append(s)
+                print(f"[bench] {json.dumps(s)}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(cfg, a.cpu_seconds)
+        print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
+
+    traffic_val = None
+    prof = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    if os.path.exists(prof):
+        try:
+            with open(prof) as f:
+                pj = json.load(f)
+            if pj.get("kernel_source_hash") == kernel_source_hash():
+                traffic_val = pj.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic_val = None
+
+    line = {
+        "metric": "decode head-steps/s + achieved HBM GB/s vs 8 TB/s peak, GDN h=32 d=128",
+        "value": head["head_steps_per_s"],
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "global_batch": cfg.batch, "v_heads": cfg.H_v,
+                   "qk_heads": cfg.H_k, "d_k": cfg.d, "d_v": cfg.d, "state": cfg.state_dtype,
+                   "merge_interval": cfg.L, "parallelism": "single-gpu"},
+        "tokens_per_s": head["tokens_per_s"],
+        "roofline": {"bound": "hbm", "achieved": head["decode_GBps"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": head["decode_GBps"] / PEAK_HBM_GBS,
+                     "traffic": traffic_val,
+                     "kernel": "dl_step_kernel (decode, append/merge)",
+                     "bytes_per_launch": head["decode_bytes_per_launch"],
+                     "launch_us_avg": head["decode_launch_us_avg"]},
+        "cpu_baseline": cpu,
+        "eager_baseline": eager_head,
+        "workloads": extras,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
