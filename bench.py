@@ -283,6 +283,33 @@ def cpu_baseline(cfg, seconds: float):
             "host_cpus": os.cpu_count()}
 
 
+def stream_reference(torch, mib: int = 1024, reps: int = 10):
+    """Device bandwidth of plain streaming kernels on this GPU (context for the
+    roofline): a 1 GiB copy (read + write) and a read-only reduction."""
+    n = mib << 20
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    a.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    e0.record()
+    for _ in range(reps):
+        a.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": copy_gbs, "read_GBps": read_gbs, "bytes": n, "kernels": "torch copy_ / sum"}
+
+
 def extra_cfg(tag: str):
     from workloads import CONFIGS, headline_gdn
     if tag.startswith("g"):
@@ -321,6 +348,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    stream_ref = stream_reference(torch)
+    print(f"[bench] stream reference {json.dumps(stream_ref)}", file=sys.stderr, flush=True)
     r = time_workload(cfg, False, steps, warmup, 1, distinct, torch, dl, native)
     head = summarize(cfg, r, steps, "deltalog")
     print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
@@ -390,6 +419,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "eager_baseline": eager_head,
         "workloads": extras,
+        "stream_reference": stream_ref,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

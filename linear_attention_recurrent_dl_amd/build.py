@@ -52,7 +52,7 @@ def _compile(src: str, extra: list) -> str:
 
 
 def build(jobs: int = 0, extra: list = None, verbose: bool = True) -> str:
-    extra = list(extra or [])
+    extra = list(extra or []) + os.environ.get("DL_EXTRA_CFLAGS", "").split()
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)

@@ -69,6 +69,10 @@ int validate_desc(const dl_pool_desc *d) {
     if (d->d_k != d->d_v || !supported_dim(d->d_k))
         return fail(DL_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d not built (need d_k == d_v in {16,32,64,128})",
                     d->d_k, d->d_v);
+    if (dl::log_stage_bytes(d->d_k, d->merge_interval - 1, d->decay) > dl::kMaxLogStageBytes)
+        return fail(DL_ERR_UNSUPPORTED, "merge_interval %d with d=%d needs %zu B of LDS for the live log (limit %zu)",
+                    d->merge_interval, d->d_k, dl::log_stage_bytes(d->d_k, d->merge_interval - 1, d->decay),
+                    dl::kMaxLogStageBytes);
     const long long units = (long long)d->max_batch * d->num_v_heads;
     if (units > (1LL << 30)) return fail(DL_ERR_INVALID_ARG, "max_batch * num_v_heads too large");
     return DL_OK;
@@ -191,7 +195,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const int mode = C == 0 ? dl::MODE_EAGER : dl::MODE_STEP;
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
-        const size_t shmem = (size_t)C * D * sizeof(float);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, C, d.decay);
         dl::StepParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -340,7 +344,7 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
-        const size_t shmem = (size_t)C * d.d_k * sizeof(float);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, C, d.decay);
         for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);
             p.nunits = cnt * d.num_v_heads;

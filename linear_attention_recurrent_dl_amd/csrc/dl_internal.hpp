@@ -56,6 +56,14 @@ struct AssignParams {
     int32_t slots[kMaxLaunchSlots];
 };
 
+// Dynamic LDS of a decode / merge block: the live log staged as fp32 -- key
+// factors [C][D], value factors [C][D] and, for per-key decay, the snapshots
+// [C][D].  Pools whose log would need more than kMaxLogStageBytes are refused.
+constexpr size_t kMaxLogStageBytes = 56 * 1024;
+inline size_t log_stage_bytes(int D, int C, int decay) {
+    return (size_t)C * D * sizeof(float) * (decay == DECAY_PER_KEY ? 3 : 2);
+}
+
 // Threads per block of the decode kernels for a head dim and state dtype.
 int block_threads(int D, int state_dtype);
 

@@ -133,6 +133,17 @@ __device__ __forceinline__ uint4 pack_16(const float (&x)[N]) {
     return make_uint4(ws[0], ws[1], ws[2], ws[3]);
 }
 
+// Row access of a tile: uniform byte base plus a 32-bit per-lane byte offset,
+// so a thread's RPT loads and stores use one offset register (scalar-base
+// addressing) instead of one 64-bit address per row.
+__device__ __forceinline__ uint4 ld16(const void *base, uint32_t off) {
+    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + off);
+}
+
+__device__ __forceinline__ void st16(void *base, uint32_t off, const uint4 &v) {
+    *reinterpret_cast<uint4 *>(static_cast<char *>(base) + off) = v;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -158,17 +169,34 @@ struct Tile {
     static constexpr int RPT = (D + RG - 1) / RG;          // rows per thread
     static constexpr int NW = NT / 64;                     // waves per block
     static constexpr bool RAGGED = RG > D;                 // some row groups own no row
-    static_assert(D % VEC == 0 && NT % CG == 0 && CG <= 64, "tile geometry");
+    static constexpr int TPE = D / 4;                      // threads per log entry (4 keys each)
+    static constexpr int EPP = NT / TPE;                   // log entries per coefficient pass
+    static constexpr int PF = D >= 128 ? 4 : 8;            // log chunks per thread loaded up front
+    static_assert(D % VEC == 0 && NT % CG == 0 && CG <= 64 && TPE <= 64, "tile geometry");
 };
+
+template <typename T, int N>
+__device__ __forceinline__ void store_lds(float *dst, const uint4 &w) {
+    float x[N];
+    unpack_f32<T, N>(w, x);
+#pragma unroll
+    for (int c = 0; c < N; c += 4)
+        *reinterpret_cast<float4 *>(dst + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+}
 
 template <int D, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, ST>::NT))
 dl_step_kernel(const StepParams p) {
     using G = Tile<D, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
-    constexpr int VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    constexpr int TPE = G::TPE, EPP = G::EPP, PF = G::PF;
+    constexpr int KV = 16 / (int)sizeof(IT);      // key-factor elements per 16-byte chunk
+    constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte chunk
     constexpr bool TOKEN = MODE != MODE_MERGE;
     constexpr bool LOG = MODE != MODE_EAGER;
+    constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
+    constexpr bool SCALAR = DECAY == DECAY_SCALAR;
 
     __shared__ float s_q[D];        // e^{l'} * q
     __shared__ float s_k[D];        // e^{l'} * k
@@ -179,9 +207,10 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_b[D];        // b (merge broadcast)
     __shared__ float s_cq[kMaxLogCap + 1];
     __shared__ float s_ck[kMaxLogCap + 1];
+    __shared__ float s_lam[kMaxLogCap + 1];   // scalar snapshots
     __shared__ float s_red[NW][2][D];
     __shared__ float s_s;           // a . q
-    extern __shared__ float s_kt[]; // [C][D] merge-time key factors e^{l'-Lam_i} * K_i
+    extern __shared__ float4 s_dyn[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -194,6 +223,10 @@ dl_step_kernel(const StepParams p) {
     const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
     const int cg = tid % CG, rg = tid / CG;
 
+    float *s_lk = reinterpret_cast<float *>(s_dyn);     // [C][D]: K_i, then e^{l'-Lam_i} * K_i
+    float *s_lu = s_lk + C * D;                         // [C][D]: U_i
+    float *s_ll = s_lu + C * D;                         // [C][D]: Lam_i (per key)
+
     int n = 0;
     if constexpr (LOG) n = p.nlog[sh];
     if constexpr (MODE == MODE_MERGE) {
@@ -201,92 +234,154 @@ dl_step_kernel(const StepParams p) {
     }
     const bool merge = (MODE != MODE_STEP) || (n == C);
 
-    // 1. base tile -> registers
-    const ST *base = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D);
-    uint4 tile[RPT];
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int r = rg + RG * j;
-        if (!G::RAGGED || r < D) tile[j] = *reinterpret_cast<const uint4 *>(base + r * D + cg * VEC);
-        else tile[j] = make_uint4(0, 0, 0, 0);
-    }
-
     const IT *klog = reinterpret_cast<const IT *>(p.klog);
     const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
     const float *lamlog = p.lamlog;
 
-    // 2. decay bookkeeping and decayed q, k
+    // ---- 1. every load of the block is issued before any is consumed:
+    //         token inputs, the whole live log, then the base tile.
+    float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
+    IT kraw{};
     if (tid < D) {
-        float lbar = 0.f, lam = 0.f;
-        if constexpr (DECAY == DECAY_SCALAR) {
-            if (LOG && n > 0) lbar = lamlog[sh * C + (n - 1)];
-            if (TOKEN) lam = p.lam[(size_t)e * H_v + h];
-        } else if constexpr (DECAY == DECAY_PER_KEY) {
-            if (LOG && n > 0) lbar = lamlog[(sh * C + (n - 1)) * D + tid];
-            if (TOKEN) lam = p.lam[((size_t)e * H_v + h) * D + tid];
+        if constexpr (TOKEN) {
+            const size_t qo = ((size_t)e * p.H_k + g) * D + tid;
+            qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+            kraw = reinterpret_cast<const IT *>(p.k)[qo];
+            kv = to_f32(kraw);
+            vv = to_f32(reinterpret_cast<const IT *>(p.v)[((size_t)e * H_v + h) * D + tid]);
+            if constexpr (SCALAR) lam = p.lam[(size_t)e * H_v + h];
+            if constexpr (PERKEY) lam = p.lam[((size_t)e * H_v + h) * D + tid];
+            if constexpr (DELTA) beta = p.beta[(size_t)e * H_v + h];
         }
-        const float lp = lbar + lam;
+        if (LOG && n > 0) {
+            if constexpr (SCALAR) lbar = lamlog[sh * C + (n - 1)];
+            if constexpr (PERKEY) lbar = lamlog[(sh * C + (n - 1)) * D + tid];
+        }
+    }
+    if constexpr (SCALAR && LOG) {
+        if (tid < n) lam_i = lamlog[sh * C + tid];
+    }
+    // live log as 16-byte chunks: K entries (of the shared q/k head), U entries,
+    // per-key snapshots; each region is contiguous for entries 0 .. n-1
+    const int cK = LOG ? n * D / KV : 0;
+    const int cU = LOG ? n * D / UV : 0;
+    const int cL = (LOG && PERKEY) ? n * D / 4 : 0;
+    const int ctot = cK + cU + cL;
+    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gk * C * D);
+    const uint4 *ub = reinterpret_cast<const uint4 *>(ulog + sh * C * D);
+    const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + sh * C * D);
+    auto chunk_ptr = [&](int x) -> const uint4 * {
+        return x < cK ? kb + x : (x < cK + cU ? ub + (x - cK) : lb + (x - cK - cU));
+    };
+    auto stage = [&](int x, const uint4 &w) {
+        if (x < cK) store_lds<IT, KV>(s_lk + x * KV, w);
+        else if (x < cK + cU) store_lds<BT, UV>(s_lu + (x - cK) * UV, w);
+        else store_lds<float, 4>(s_ll + (x - cK - cU) * 4, w);
+    };
+    uint4 pf[PF];
+    if constexpr (LOG) {
+#pragma unroll
+        for (int m = 0; m < PF; ++m) {
+            const int x = tid + m * NT;
+            if (x < ctot) pf[m] = *chunk_ptr(x);
+        }
+    }
+    // base tile of this slot-head; a thread reads rows rg + RG * j
+    const ST *tbase = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D);
+    const uint32_t toff = (uint32_t)((rg * D + cg * VEC) * sizeof(ST));
+    constexpr uint32_t TROW = RG * D * sizeof(ST);      // bytes between a thread's rows
+    uint4 tile[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        if (!G::RAGGED || rg + RG * j < D) tile[j] = ld16(tbase, toff + j * TROW);
+        else tile[j] = make_uint4(0, 0, 0, 0);
+    }
+
+    // ---- 2. decay bookkeeping, decayed q / k, and the log into LDS
+    if (tid < D) {
+        const float lp = lbar + lam;                    // l' = l_bar + lambda
         const float gg = (DECAY == DECAY_NONE) ? 1.f : __expf(lp);
         s_lp[tid] = lp;
         s_g[tid] = gg;
         if constexpr (TOKEN) {
-            const size_t qo = ((size_t)e * p.H_k + g) * D + tid;
-            const float qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
-            const float kv = to_f32(reinterpret_cast<const IT *>(p.k)[qo]);
             s_qr[tid] = qv;
             s_a[tid] = kv;
             s_q[tid] = gg * qv;
             s_k[tid] = gg * kv;
         }
     }
+    if constexpr (LOG) {
+        if constexpr (SCALAR) {
+            if (tid < n) s_lam[tid] = lam_i;
+        }
+#pragma unroll
+        for (int m = 0; m < PF; ++m) {
+            const int x = tid + m * NT;
+            if (x < ctot) stage(x, pf[m]);
+        }
+        for (int x = tid + PF * NT; x < ctot; x += NT) stage(x, *chunk_ptr(x));   // long logs
+    }
     __syncthreads();
 
-    // 3. replay coefficients (one wave per live entry) and a . q
-    for (int i = wave; i <= n; i += NW) {
-        if (i == n) {
-            if constexpr (TOKEN) {
-                float acc = 0.f;
-                for (int r = lane; r < D; r += 64) acc += s_a[r] * s_qr[r];
-                acc = wave_sum(acc);
-                if (lane == 0) s_s = acc;
-            }
-            continue;
-        }
-        const IT *Ki = klog + (gk * C + i) * D;
-        float wsc = 1.f;
-        if constexpr (DECAY == DECAY_SCALAR) wsc = __expf(s_lp[0] - lamlog[sh * C + i]);
+    // ---- 3. replay coefficients, TPE threads per entry (4 keys each):
+    //         Kt_i = e^{l' - Lam_i} * K_i (kept for a merge), c^q_i = Kt_i . q,
+    //         c^k_i = Kt_i . k; the pass that reaches i == n computes a . q
+    for (int i0 = 0; i0 <= n; i0 += EPP) {
+        const int i = i0 + tid / TPE;
+        const int r0 = (tid % TPE) * 4;
         float pq = 0.f, pk = 0.f;
-        for (int r = lane; r < D; r += 64) {
-            float w = wsc;
-            if constexpr (DECAY == DECAY_PER_KEY) w = __expf(s_lp[r] - lamlog[(sh * C + i) * D + r]);
-            const float kt = w * to_f32(Ki[r]);
-            if (merge) s_kt[i * D + r] = kt;
-            if constexpr (TOKEN) {
-                pq += kt * s_qr[r];
-                if constexpr (DELTA) pk += kt * s_a[r];
+        if (LOG && i < n) {
+            const float4 k4 = *reinterpret_cast<const float4 *>(s_lk + i * D + r0);
+            float kt[4] = {k4.x, k4.y, k4.z, k4.w};
+            if constexpr (PERKEY) {
+                const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + r0);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[r0 + j] - lv[j]);
+            } else if constexpr (SCALAR) {
+                const float w = __expf(s_lp[0] - s_lam[i]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kt[j] *= w;
             }
+            if (merge) *reinterpret_cast<float4 *>(s_lk + i * D + r0) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+            if constexpr (TOKEN) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pq += kt[j] * s_qr[r0 + j];
+                    if constexpr (DELTA) pk += kt[j] * s_a[r0 + j];
+                }
+            }
+        } else if (TOKEN && i == n) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
         }
         if constexpr (TOKEN) {
-            pq = wave_sum(pq);
-            if constexpr (DELTA) pk = wave_sum(pk);
-            if (lane == 0) {
-                s_cq[i] = pq;
-                s_ck[i] = pk;
+#pragma unroll
+            for (int off = 1; off < TPE; off <<= 1) {
+                pq += __shfl_xor(pq, off, 64);
+                if constexpr (DELTA) pk += __shfl_xor(pk, off, 64);
+            }
+            if (tid % TPE == 0) {
+                if (i < n) {
+                    s_cq[i] = pq;
+                    s_ck[i] = pk;
+                } else if (i == n) {
+                    s_s = pq;
+                }
             }
         }
     }
     __syncthreads();
 
-    // 4-6. projections, value factor, output, append commit
+    // ---- 4-6. projections, value factor, output, append commit
     if constexpr (TOKEN) {
         float accq[VEC], acck[VEC];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) accq[c] = acck[c] = 0.f;
         if constexpr (LOG) {
             for (int i = rg; i < n; i += RG) {             // log entries as extra rows
-                float u[VEC];
-                load_f32<BT, VEC>(ulog + (sh * C + i) * D + cg * VEC, u);
                 const float cq = s_cq[i], ck = s_ck[i];
+                const float *u = s_lu + i * D + cg * VEC;
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) {
                     accq[c] += cq * u[c];
@@ -333,12 +428,10 @@ dl_step_kernel(const StepParams p) {
                 yq += s_red[w][0][tid];
                 yk += s_red[w][1][tid];
             }
-            const size_t vo = ((size_t)e * H_v + h) * D + tid;
-            const float vin = to_f32(reinterpret_cast<const IT *>(p.v)[vo]);
             float b;
-            if constexpr (DELTA) b = p.beta[(size_t)e * H_v + h] * (vin - yk);
-            else b = vin;
-            p.out[vo] = yq + s_s * b;
+            if constexpr (DELTA) b = beta * (vv - yk);
+            else b = vv;
+            p.out[((size_t)e * H_v + h) * D + tid] = yq + s_s * b;
             if (merge) {
                 s_b[tid] = b;
             } else if constexpr (LOG) {
@@ -346,10 +439,10 @@ dl_step_kernel(const StepParams p) {
                 ulw[(sh * C + n) * D + tid] = from_f32<BT>(b);
                 if (h % grp == 0) {                        // designated writer of the key entry
                     IT *klw = reinterpret_cast<IT *>(p.klog);
-                    klw[(gk * C + n) * D + tid] = reinterpret_cast<const IT *>(p.k)[((size_t)e * p.H_k + g) * D + tid];
+                    klw[(gk * C + n) * D + tid] = kraw;
                 }
-                if constexpr (DECAY == DECAY_PER_KEY) p.lamlog[(sh * C + n) * D + tid] = s_lp[tid];
-                if constexpr (DECAY == DECAY_SCALAR) {
+                if constexpr (PERKEY) p.lamlog[(sh * C + n) * D + tid] = s_lp[tid];
+                if constexpr (SCALAR) {
                     if (tid == 0) p.lamlog[sh * C + n] = s_lp[0];
                 }
             }
@@ -360,7 +453,7 @@ dl_step_kernel(const StepParams p) {
     }
     if (!merge) return;
 
-    // merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T, from registers
+    // ---- merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T, from registers
     __syncthreads();
     float acc[RPT][VEC];
     float bcol[VEC];
@@ -379,21 +472,27 @@ dl_step_kernel(const StepParams p) {
     if constexpr (LOG) {
         for (int i = 0; i < n; ++i) {
             float u[VEC];
-            load_f32<BT, VEC>(ulog + (sh * C + i) * D + cg * VEC, u);
+#pragma unroll
+            for (int c = 0; c < VEC; c += 4) {
+                const float4 u4 = *reinterpret_cast<const float4 *>(s_lu + i * D + cg * VEC + c);
+                u[c] = u4.x;
+                u[c + 1] = u4.y;
+                u[c + 2] = u4.z;
+                u[c + 3] = u4.w;
+            }
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int r = rg + RG * j;
-                const float kt = s_kt[i * D + (r < D ? r : 0)];
+                const float kt = s_lk[i * D + (r < D ? r : 0)];
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[j][c] += kt * u[c];
             }
         }
     }
-    ST *basew = reinterpret_cast<ST *>(p.base) + sh * (size_t)(D * D);
+    ST *basew = const_cast<ST *>(tbase);
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-        const int r = rg + RG * j;
-        if (!G::RAGGED || r < D) *reinterpret_cast<uint4 *>(basew + r * D + cg * VEC) = pack_16<ST, VEC>(acc[j]);
+        if (!G::RAGGED || rg + RG * j < D) st16(basew, toff + j * TROW, pack_16<ST, VEC>(acc[j]));
     }
 }
 
