@@ -42,12 +42,8 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrent_dl_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()[:16]
+    from linear_attention_recurrent_dl_amd.rocprof_summary import kernel_source_hash as ksh
+    return ksh()
 
 
 def parse(argv=None):
@@ -55,7 +51,9 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", type=int, default=2, help="headline workload index (1-5)")
+    ap.add_argument("--workload", default="2",
+                    help="headline workload: config index 1-5, or gB = GDN fp32 d=128 at batch B")
+    ap.add_argument("--rotate", type=int, default=1, help="independent pools decoded in rotation (headline)")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
     ap.add_argument("--extra", default="3,4,5,g64,g128,g256,g512",
                     help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
@@ -201,6 +199,18 @@ class Staged:
         self.bank = None
 
 
+def event_pair_overhead_ms(torch, reps: int = 200) -> float:
+    """Average elapsed time of two events recorded back to back on the stream
+    (no kernel between): the fixed cost inside every per-launch event pair."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
 def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native):
     st = Staged(cfg, eager, rotate, distinct, torch, dl, native)
     try:
@@ -226,12 +236,16 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
         torch.cuda.empty_cache()
 
 
+EVENT_OVERHEAD_MS = 0.0
+
+
 def summarize(cfg, r, steps, tag):
     from linear_attention_recurrent_dl_amd import traffic
     ms_step = r["total_ms"] / steps
     head_steps = cfg.batch * cfg.H_v * steps
-    avg_launch_ms = float(np.mean(r["launch_ms"]))
-    med_launch_ms = float(np.median(r["launch_ms"]))
+    raw_launch_ms = float(np.mean(r["launch_ms"]))
+    avg_launch_ms = max(raw_launch_ms - EVENT_OVERHEAD_MS, 1e-6)
+    med_launch_ms = float(np.median(r["launch_ms"])) - EVENT_OVERHEAD_MS
     bytes_per_launch = r["dec_bytes"] / steps
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
@@ -243,6 +257,7 @@ def summarize(cfg, r, steps, tag):
         "head_steps_per_s": head_steps / (r["total_ms"] * 1e-3),
         "tokens_per_s": cfg.batch * steps / (r["total_ms"] * 1e-3),
         "decode_launch_us_avg": avg_launch_ms * 1e3, "decode_launch_us_median": med_launch_ms * 1e3,
+        "decode_launch_us_raw_event_pair": raw_launch_ms * 1e3,
         "decode_bytes_per_launch": bytes_per_launch,
         "decode_GBps": achieved, "decode_frac_of_8TBps": achieved / PEAK_HBM_GBS,
         "model_bytes_per_head_step": (traffic.eager_head_step_bytes(sh) if tag == "eager"
@@ -336,7 +351,7 @@ def main(argv=None) -> int:
         return 1
     native.lib()
     torch.cuda.set_device(0)
-    cfg = CONFIGS[a.workload]
+    cfg = extra_cfg(a.workload)
     steps, warmup = a.steps, a.warmup
     distinct = a.distinct_steps or min(steps + warmup, 4 * cfg.L)
     print(f"[bench] headline {cfg.describe()} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
@@ -348,14 +363,16 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    global EVENT_OVERHEAD_MS
+    EVENT_OVERHEAD_MS = event_pair_overhead_ms(torch)
     stream_ref = stream_reference(torch)
     print(f"[bench] stream reference {json.dumps(stream_ref)}", file=sys.stderr, flush=True)
-    r = time_workload(cfg, False, steps, warmup, 1, distinct, torch, dl, native)
+    r = time_workload(cfg, False, steps, warmup, a.rotate, distinct, torch, dl, native)
     head = summarize(cfg, r, steps, "deltalog")
     print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
     eager_head = None
     if not a.no_eager:
-        re_ = time_workload(cfg, True, steps, warmup, 1, min(distinct, 64), torch, dl, native)
+        re_ = time_workload(cfg, True, steps, warmup, a.rotate, min(distinct, 64), torch, dl, native)
         eager_head = summarize(cfg, re_, steps, "eager")
         print(f"[bench] {json.dumps(eager_head)}", file=sys.stderr, flush=True)
 
@@ -383,7 +400,7 @@ def main(argv=None) -> int:
         print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
 
     traffic_val = None
-    prof = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    prof = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_r{a.rotate}.json")
     if os.path.exists(prof):
         try:
             with open(prof) as f:
@@ -406,16 +423,19 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "global_batch": cfg.batch, "v_heads": cfg.H_v,
+        "config": {"workload": cfg.name, "rotated_pools": a.rotate, "global_batch": cfg.batch, "v_heads": cfg.H_v,
                    "qk_heads": cfg.H_k, "d_k": cfg.d, "d_v": cfg.d, "state": cfg.state_dtype,
                    "merge_interval": cfg.L, "parallelism": "single-gpu"},
         "tokens_per_s": head["tokens_per_s"],
         "roofline": {"bound": "hbm", "achieved": head["decode_GBps"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["decode_GBps"] / PEAK_HBM_GBS,
                      "traffic": traffic_val,
+                     "traffic_source": os.path.relpath(prof, ROOT) if traffic_val is not None else None,
                      "kernel": "dl_step_kernel (decode, append/merge)",
                      "bytes_per_launch": head["decode_bytes_per_launch"],
-                     "launch_us_avg": head["decode_launch_us_avg"]},
+                     "launch_us_avg": head["decode_launch_us_avg"],
+                     "launch_us_raw_event_pair": head["decode_launch_us_raw_event_pair"],
+                     "event_pair_overhead_us": EVENT_OVERHEAD_MS * 1e3},
         "cpu_baseline": cpu,
         "eager_baseline": eager_head,
         "workloads": extras,

@@ -155,7 +155,7 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids,
  * A slot whose log holds L-1 entries takes the merge step: its output is
  * computed from base + log + this token, and the base is rewritten with the
  * materialized state; its log becomes empty.  Any other slot appends this
- * token's (a_t, b_t, snapshot) at log index n and leaves the base unread-only. */
+ * token's (a_t, b_t, snapshot) at log index n and leaves the base unchanged. */
 int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
                    const void *q, const void *a_or_k, const void *b_or_v,
                    const float *lambda, const float *beta, float *out, void *stream);

@@ -2,11 +2,17 @@
 
     python -m linear_attention_recurrent_dl_amd.rocprof_summary trace  <results.db | kernel_trace.csv>
     python -m linear_attention_recurrent_dl_amd.rocprof_summary pmc    <results.db | counter_collection.csv> COUNTER
+    python -m linear_attention_recurrent_dl_amd.rocprof_summary traffic FETCH_DB WRITE_DB KERNEL_SUBSTR COPY_BYTES [OUT.json]
 
 ``trace`` prints count / average / min / max duration per kernel name;
 ``pmc`` prints, per kernel name, the average value of COUNTER per dispatch and
-the number of dispatches.  Works on the SQLite database rocprofv3 writes by
-default (``*_results.db``) and on its CSV output.
+the number of dispatches.  ``traffic`` turns a FETCH_SIZE run and a
+WRITE_SIZE run into HBM bytes per launch of the kernel whose name contains
+KERNEL_SUBSTR: each counter (KiB per dispatch) is scaled by the factor that
+maps the same counter of a plain device copy of COPY_BYTES bytes (the largest
+copy kernel in the run, which reads and writes COPY_BYTES each) onto its known
+size.  Works on the SQLite database rocprofv3 writes by default
+(``*_results.db``) and on its CSV output.
 """
 
 from __future__ import annotations
@@ -41,6 +47,23 @@ def trace_rows(path: str):
     return sorted(rows, key=lambda r: -r[5])
 
 
+def pmc_dispatches(path: str, counter: str):
+    """{kernel name: [value of COUNTER per dispatch]}."""
+    per = defaultdict(lambda: defaultdict(float))
+    if path.endswith(".db"):
+        con = sqlite3.connect(path)
+        rows = con.execute("select kernel_name, dispatch_id, counter_value from counters_collection "
+                           "where counter_name = ?", (counter,)).fetchall()
+        for name, did, val in rows:
+            per[name][did] += float(val)
+    else:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {n: list(d.values()) for n, d in per.items()}
+
+
 def pmc_rows(path: str, counter: str):
     """[(name, dispatches, avg value per dispatch)]."""
     per = defaultdict(lambda: defaultdict(float))     # name -> dispatch -> value
@@ -68,6 +91,54 @@ def pmc_rows(path: str, counter: str):
     return sorted(out, key=lambda r: -r[2] * r[1])
 
 
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int) -> dict:
+    f_rows = pmc_rows(fetch_path, "FETCH_SIZE")
+    w_rows = pmc_rows(write_path, "WRITE_SIZE")
+
+    def pick(rows, sub):
+        m = [r for r in rows if sub in r[0]]
+        if not m:
+            raise SystemExit(f"no kernel matching {sub!r}")
+        return max(m, key=lambda r: r[1])          # most dispatches
+
+    def copy_row(path, counter):
+        # the single largest dispatch of a copy kernel: the calibration copy
+        best = None
+        for name, vals in pmc_dispatches(path, counter).items():
+            if "copy" in name.lower():
+                v = max(vals)
+                if best is None or v > best[2]:
+                    best = (name, 1, v)
+        return best
+
+    kf, kw = pick(f_rows, kernel), pick(w_rows, kernel)
+    cf, cw = copy_row(fetch_path, "FETCH_SIZE"), copy_row(write_path, "WRITE_SIZE")
+    f_scale = copy_bytes / (cf[2] * 1024.0) if cf else 1.0
+    w_scale = copy_bytes / (cw[2] * 1024.0) if cw else 1.0
+    fetch_b = kf[2] * 1024.0 * f_scale
+    write_b = kw[2] * 1024.0 * w_scale
+    return {"kernel": kf[0], "dispatches": kf[1], "fetch_kib_per_dispatch": kf[2],
+            "write_kib_per_dispatch": kw[2], "copy_kernel": cf[0] if cf else None,
+            "copy_fetch_kib": cf[2] if cf else None, "copy_write_kib": cw[2] if cw else None,
+            "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+            "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+            "hbm_bytes_per_launch": fetch_b + write_b, "kernel_source_hash": kernel_source_hash()}
+
+
 def main(argv=None) -> int:
     argv = sys.argv[1:] if argv is None else argv
     if len(argv) < 2:
@@ -84,6 +155,14 @@ def main(argv=None) -> int:
         print(f"{'kernel':100s} {'dispatches':>10s} {counter + '/dispatch':>20s}")
         for n, c, v in pmc_rows(path, counter):
             print(f"{_short(n):100s} {c:10d} {v:20.1f}")
+    elif mode == "traffic":
+        import json
+        t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
+        txt = json.dumps(t, indent=1)
+        print(txt)
+        if len(argv) > 5:
+            with open(argv[5], "w") as f:
+                f.write(txt + "\n")
     else:
         print(__doc__)
         return 2
