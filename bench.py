@@ -54,6 +54,8 @@ def parse(argv=None):
     ap.add_argument("--workload", default="2",
                     help="headline workload: config index 1-5, or gB = GDN fp32 d=128 at batch B")
     ap.add_argument("--rotate", type=int, default=1, help="independent pools decoded in rotation (headline)")
+    ap.add_argument("--value-tile", type=int, default=0,
+                    help="value-tile width B_V for the headline pools (0 = library default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
     ap.add_argument("--extra", default="3,4,5,g64,g128,g256,g512",
                     help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
@@ -61,6 +63,7 @@ def parse(argv=None):
     ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline runs")
     ap.add_argument("--rotate-bytes", type=float, default=1.25 * 2 ** 30,
                     help="minimum bytes of pools rotated per extra workload (cold cache)")
+    ap.add_argument("--no-graph", action="store_true", help="launch mode only (no HIP-graph replay)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -74,7 +77,7 @@ def parse(argv=None):
 class Staged:
     """A workload's pools and device-resident step inputs, ready to launch."""
 
-    def __init__(self, cfg, eager: bool, rotate: int, distinct: int, torch, dl, native):
+    def __init__(self, cfg, eager: bool, rotate: int, distinct: int, torch, dl, native, value_tile: int = 0):
         from workloads import Workload
         from linear_attention_recurrent_dl_amd import traffic
 
@@ -89,8 +92,10 @@ class Staged:
         self.shape = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update,
                                        cfg.state_dtype, cfg.in_dtype, L)
         self.pools = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
-                                      cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch)
+                                      cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch,
+                                      value_tile=value_tile)
                       for _ in range(rotate)]
+        self.value_tile = self.pools[0].value_tile
         self.shadow = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
                                        cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch, device=None)
                        for _ in range(rotate)]
@@ -199,20 +204,13 @@ class Staged:
         self.bank = None
 
 
-def event_pair_overhead_ms(torch, reps: int = 200) -> float:
-    """Average elapsed time of two events recorded back to back on the stream
-    (no kernel between): the fixed cost inside every per-launch event pair."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-
-def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native):
-    st = Staged(cfg, eager, rotate, distinct, torch, dl, native)
+def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native, value_tile=0, graph=True):
+    """Launch mode: W warm-up steps, then K steps each bracketed by a HIP event
+    pair on the launch stream.  Graph mode: the staged steps captured once in a
+    HIP graph (the kernels read the live-log lengths on the device, so the
+    same capture is valid for every replay), replayed until about K steps ran,
+    timed by an event pair around the replays."""
+    st = Staged(cfg, eager, rotate, distinct, torch, dl, native, value_tile)
     try:
         st.plan_bytes(0, warmup)                 # advance the shadow schedule past warm-up
         st.run(0, warmup)
@@ -227,43 +225,92 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
         t_end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        total_ms = t_start.elapsed_time(t_end)
-        launch_ms = [a.elapsed_time(b) for a, b in ev]
-        return dict(total_ms=total_ms, wall_s=wall, launch_ms=launch_ms, dec_bytes=dec_bytes,
-                    asg_bytes=asg_bytes, L=st.L)
+        out = dict(total_ms=t_start.elapsed_time(t_end), wall_s=wall,
+                   launch_ms=[a.elapsed_time(b) for a, b in ev], dec_bytes=dec_bytes,
+                   asg_bytes=asg_bytes, L=st.L, value_tile=st.value_tile, steps=steps)
+        if graph:
+            S = len(st.inputs)
+            t0 = warmup + steps
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st.run(t0, S)
+            reps = max(1, int(round(steps / S)))
+            st.plan_bytes(t0, S)                 # the warm-up replay
+            g.replay()
+            torch.cuda.synchronize()
+            gb_dec, gb_asg = 0.0, 0.0
+            for _ in range(reps):
+                a, b = st.plan_bytes(t0, S)
+                gb_dec += a
+                gb_asg += b
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out["graph"] = dict(ms=e0.elapsed_time(e1), steps=reps * S, dec_bytes=gb_dec, asg_bytes=gb_asg)
+            del g
+        return out
     finally:
         st.close()
         torch.cuda.empty_cache()
 
 
-EVENT_OVERHEAD_MS = 0.0
-
-
 def summarize(cfg, r, steps, tag):
     from linear_attention_recurrent_dl_amd import traffic
-    ms_step = r["total_ms"] / steps
-    head_steps = cfg.batch * cfg.H_v * steps
-    raw_launch_ms = float(np.mean(r["launch_ms"]))
-    avg_launch_ms = max(raw_launch_ms - EVENT_OVERHEAD_MS, 1e-6)
-    med_launch_ms = float(np.median(r["launch_ms"])) - EVENT_OVERHEAD_MS
-    bytes_per_launch = r["dec_bytes"] / steps
-    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
                            cfg.in_dtype, r["L"])
-    return {
+    launch_ms = float(np.mean(r["launch_ms"]))
+    bytes_per_launch = r["dec_bytes"] / steps
+    res = {
         "workload": cfg.name, "kernel": tag, "batch": cfg.batch, "H_v": cfg.H_v, "H_k": cfg.H_k,
-        "d": cfg.d, "L": r["L"], "state": cfg.state_dtype,
-        "ms_per_step": ms_step,
-        "head_steps_per_s": head_steps / (r["total_ms"] * 1e-3),
-        "tokens_per_s": cfg.batch * steps / (r["total_ms"] * 1e-3),
-        "decode_launch_us_avg": avg_launch_ms * 1e3, "decode_launch_us_median": med_launch_ms * 1e3,
-        "decode_launch_us_raw_event_pair": raw_launch_ms * 1e3,
+        "d": cfg.d, "L": r["L"], "state": cfg.state_dtype, "value_tile": r["value_tile"],
         "decode_bytes_per_launch": bytes_per_launch,
-        "decode_GBps": achieved, "decode_frac_of_8TBps": achieved / PEAK_HBM_GBS,
         "model_bytes_per_head_step": (traffic.eager_head_step_bytes(sh) if tag == "eager"
                                       else traffic.deltalog_model_bytes(sh)),
         "assign_bytes_per_step": r["asg_bytes"] / steps,
+        # launch mode: one host call per step, an event pair around every launch
+        "launch_mode": {
+            "ms_per_step": r["total_ms"] / steps,
+            "head_steps_per_s": cfg.batch * cfg.H_v * steps / (r["total_ms"] * 1e-3),
+            "decode_event_pair_us_avg": launch_ms * 1e3,
+            "decode_event_pair_us_median": float(np.median(r["launch_ms"])) * 1e3,
+            "decode_GBps_event_pair": bytes_per_launch / (launch_ms * 1e-3) / 1e9,
+        },
     }
+    gr = r.get("graph")
+    if gr:
+        ms_step = gr["ms"] / gr["steps"]
+        res.update({
+            "ms_per_step": ms_step,
+            "head_steps_per_s": cfg.batch * cfg.H_v * gr["steps"] / (gr["ms"] * 1e-3),
+            "tokens_per_s": cfg.batch * gr["steps"] / (gr["ms"] * 1e-3),
+        })
+        if gr["asg_bytes"] == 0:
+            # a step is exactly one decode launch: graph time per step is its duration
+            dec_us = ms_step * 1e3
+            res["decode_launch_us"] = dec_us
+            res["decode_launch_source"] = "graph replay, back-to-back launches"
+            bpl = gr["dec_bytes"] / gr["steps"]
+            res["decode_bytes_per_launch"] = bpl
+        else:
+            dec_us = launch_ms * 1e3
+            res["decode_launch_us"] = dec_us
+            res["decode_launch_source"] = "event pair per launch (step also assigns fresh slots)"
+            bpl = bytes_per_launch
+    else:
+        res.update({"ms_per_step": r["total_ms"] / steps,
+                    "head_steps_per_s": res["launch_mode"]["head_steps_per_s"],
+                    "tokens_per_s": cfg.batch * steps / (r["total_ms"] * 1e-3)})
+        dec_us = launch_ms * 1e3
+        res["decode_launch_us"] = dec_us
+        res["decode_launch_source"] = "event pair per launch"
+        bpl = bytes_per_launch
+    res["decode_GBps"] = bpl / (dec_us * 1e-6) / 1e9
+    res["decode_frac_of_8TBps"] = res["decode_GBps"] / PEAK_HBM_GBS
+    return res
 
 
 def cpu_baseline(cfg, seconds: float):
@@ -363,16 +410,16 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    global EVENT_OVERHEAD_MS
-    EVENT_OVERHEAD_MS = event_pair_overhead_ms(torch)
     stream_ref = stream_reference(torch)
     print(f"[bench] stream reference {json.dumps(stream_ref)}", file=sys.stderr, flush=True)
-    r = time_workload(cfg, False, steps, warmup, a.rotate, distinct, torch, dl, native)
+    r = time_workload(cfg, False, steps, warmup, a.rotate, distinct, torch, dl, native, a.value_tile,
+                      graph=not a.no_graph)
     head = summarize(cfg, r, steps, "deltalog")
     print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
     eager_head = None
     if not a.no_eager:
-        re_ = time_workload(cfg, True, steps, warmup, a.rotate, min(distinct, 64), torch, dl, native)
+        re_ = time_workload(cfg, True, steps, warmup, a.rotate, distinct, torch, dl, native, a.value_tile,
+                            graph=not a.no_graph)
         eager_head = summarize(cfg, re_, steps, "eager")
         print(f"[bench] {json.dumps(eager_head)}", file=sys.stderr, flush=True)
 
@@ -386,7 +433,8 @@ def main(argv=None) -> int:
             R = max(1, int(np.ceil(a.rotate_bytes / ws)))
             xs = a.extra_steps or 4 * c.L
             for eager in ([False] if a.no_eager else [False, True]):
-                rr = time_workload(c, eager, xs, c.L, R, min(4 * c.L, xs + c.L), torch, dl, native)
+                rr = time_workload(c, eager, xs, c.L, R, min(4 * c.L, xs + c.L), torch, dl, native,
+                                   graph=not a.no_graph)
                 s = summarize(c, rr, xs, "eager" if eager else "deltalog")
                 s["rotated_pools"] = R
                 s["pool_bytes"] = ws if not eager else sum(dl.dl_pool_sizes(dl.make_desc(
@@ -425,7 +473,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name, "rotated_pools": a.rotate, "global_batch": cfg.batch, "v_heads": cfg.H_v,
                    "qk_heads": cfg.H_k, "d_k": cfg.d, "d_v": cfg.d, "state": cfg.state_dtype,
-                   "merge_interval": cfg.L, "parallelism": "single-gpu"},
+                   "merge_interval": cfg.L, "value_tile": head["value_tile"], "parallelism": "single-gpu"},
         "tokens_per_s": head["tokens_per_s"],
         "roofline": {"bound": "hbm", "achieved": head["decode_GBps"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": head["decode_GBps"] / PEAK_HBM_GBS,
@@ -433,9 +481,10 @@ def main(argv=None) -> int:
                      "traffic_source": os.path.relpath(prof, ROOT) if traffic_val is not None else None,
                      "kernel": "dl_step_kernel (decode, append/merge)",
                      "bytes_per_launch": head["decode_bytes_per_launch"],
-                     "launch_us_avg": head["decode_launch_us_avg"],
-                     "launch_us_raw_event_pair": head["decode_launch_us_raw_event_pair"],
-                     "event_pair_overhead_us": EVENT_OVERHEAD_MS * 1e3},
+                     "launch_us": head["decode_launch_us"],
+                     "launch_source": head["decode_launch_source"],
+                     "launch_us_event_pair": head["launch_mode"]["decode_event_pair_us_avg"]},
+        "launch_mode": head["launch_mode"],
         "cpu_baseline": cpu,
         "eager_baseline": eager_head,
         "workloads": extras,

@@ -3,8 +3,8 @@
  *
  * Sources, cited by title and passage:
  *  [DL]   "DeltaLog: Deferred Materialization of Recurrent States for Linear
- *         Attention Decoding": Eq. 3 (the common decode step, "the common
- *         decode-time interface"), the design section (append-merge cycle,
+ *         Attention Decoding": Eq. 3 (the common decode step, which the paper
+ *         uses as the interface every operator shares), the design section (append-merge cycle,
  *         physical state, logical-state equation), the GPU-execution section
  *         (ReplayPrep / AppendDecode / Finalize, Merge), the operator
  *         instantiations (GDN, KDA, RWKV6) and the serving-integration section
@@ -79,6 +79,15 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *   decay, update   DL_DECAY_*, DL_UPDATE_*
  *   state_dtype     dense base: DL_F32 or DL_BF16
  *   in_dtype        q, k / a_t and v / b_t inputs: DL_F32 or DL_BF16
+ *   value_tile      B_V, columns of the d_k x B_V value tile one GPU work unit
+ *                   owns ([DL] GPU-execution section, value tiling); 0 picks the
+ *                   library default: 64 for an fp32 state at d = 128, else d,
+ *                   except 32 when max_batch * num_v_heads slot-heads would
+ *                   give fewer than 256 work units (d >= 64).
+ *                   Built widths: d = 128: 128, 64, 32, 16; d = 64: 64, 32;
+ *                   d = 32: 32; d = 16: 16.  Narrower tiles give more work
+ *                   units per slot (lower latency at small batch) at the cost
+ *                   of repeating the key-side replay work per tile.
  * Factor storage follows [DL]'s operator instantiations: key factors a_t are
  * stored in in_dtype (a lossless copy of the input); value factors b_t are
  * fp32 for delta operators (cancellation-sensitive) and in_dtype for plain
@@ -95,6 +104,7 @@ typedef struct {
     int32_t update;
     int32_t state_dtype;
     int32_t in_dtype;
+    int32_t value_tile;
 } dl_pool_desc;
 
 /* Device buffers of a pool, allocated by the caller with the sizes
@@ -106,7 +116,8 @@ typedef struct {
  *                                                     log-decay snapshot of entry i:
  *                                                     the cumulative log-decay right
  *                                                     after entry i's own decay
- *   nlog    [P, H_v]                    int32         live-log length per slot-head
+ *   nlog    [P, H_v, d_v / B_V]         int32         live-log length per value tile (all
+ *                                                     tiles of a slot hold the same value)
  * The cumulative log-decay l_bar of [DL]'s physical state is not stored: it
  * equals lamlog[n-1] when n > 0 and 0 when the log is empty. */
 typedef struct {
@@ -186,9 +197,13 @@ int dl_get_log_len(const dl_pool *pool, int32_t *n_out);
 int dl_schedule(const dl_pool *pool, int32_t B, const int32_t *slot_ids,
                 int32_t *merge_out, int32_t *index_out);
 
-/* Device copy of nlog, read back synchronously: n_out host int32 [P, H_v].
+/* Device copy of nlog, read back synchronously: n_out host int32
+ * [P, H_v, d_v / B_V].
  * Waits for the stream.  DL_ERR_DRY_RUN on a host-only pool. */
 int dl_read_log_len_device(dl_pool *pool, int32_t *n_out, void *stream);
+
+/* Effective value-tile width B_V of a descriptor (> 0), or a DL_ERR_* code. */
+int dl_value_tile(const dl_pool_desc *desc);
 
 /* Message of the last failed call on this host thread ("" if none). */
 const char *dl_last_error(void);

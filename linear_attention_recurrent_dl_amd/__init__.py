@@ -20,14 +20,15 @@ from ._native import DeltaLogError, DL_DECAY, DL_DTYPE, DL_UPDATE  # noqa: F401
 
 __all__ = ["dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
            "dl_decode_step", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
-           "dl_schedule", "dl_read_log_len_device", "dl_last_error", "dl_launch_slot_limit",
+           "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error", "dl_launch_slot_limit",
            "make_desc", "DeltaLogPool", "DeltaLogError"]
 
 
 def make_desc(num_slots: int, max_batch: int, H_v: int, H_k: int, d: int, L: int,
-              decay: str, update: str, state_dtype: str, in_dtype: str) -> N.dl_pool_desc:
+              decay: str, update: str, state_dtype: str, in_dtype: str,
+              value_tile: int = 0) -> N.dl_pool_desc:
     return N.dl_pool_desc(num_slots, max_batch, H_v, H_k, d, d, L, DL_DECAY[decay],
-                          DL_UPDATE[update], DL_DTYPE[state_dtype], DL_DTYPE[in_dtype])
+                          DL_UPDATE[update], DL_DTYPE[state_dtype], DL_DTYPE[in_dtype], value_tile)
 
 
 def _ids(slot_ids) -> np.ndarray:
@@ -97,8 +98,16 @@ def dl_schedule(pool: int, slot_ids):
     return merge, index
 
 
-def dl_read_log_len_device(pool: int, num_slots: int, H_v: int, stream) -> np.ndarray:
-    out = np.zeros((num_slots, H_v), dtype=np.int32)
+def dl_value_tile(desc: N.dl_pool_desc) -> int:
+    rc = N.lib().dl_value_tile(ctypes.byref(desc))
+    if rc < 0:
+        N.check(rc, "dl_value_tile")
+    return int(rc)
+
+
+def dl_read_log_len_device(pool: int, num_slots: int, H_v: int, stream, tiles: int = 1) -> np.ndarray:
+    """Live length of every value tile, [num_slots, H_v * tiles]."""
+    out = np.zeros((num_slots, H_v * tiles), dtype=np.int32)
     N.check(N.lib().dl_read_log_len_device(pool, _i32p(out), stream), "dl_read_log_len_device")
     return out
 
@@ -121,14 +130,16 @@ class DeltaLogPool:
 
     def __init__(self, num_slots: int, H_v: int, H_k: int, d: int, L: int, decay: str,
                  update: str, state_dtype: str = "f32", in_dtype: str = "f32",
-                 max_batch: Optional[int] = None, device="cuda"):
+                 max_batch: Optional[int] = None, device="cuda", value_tile: int = 0):
         self.num_slots, self.H_v, self.H_k, self.d, self.L = num_slots, H_v, H_k, d, L
         self.decay, self.update = decay, update
         self.state_dtype, self.in_dtype = state_dtype, in_dtype
         self.max_batch = max_batch or num_slots
         self.desc = make_desc(num_slots, self.max_batch, H_v, H_k, d, L, decay, update,
-                              state_dtype, in_dtype)
+                              state_dtype, in_dtype, value_tile)
         self.sizes = dl_pool_sizes(self.desc)
+        self.value_tile = dl_value_tile(self.desc)
+        self.tiles = d // self.value_tile
         self.device = device
         self.bufs = {}
         if device is None:
@@ -167,7 +178,8 @@ class DeltaLogPool:
         return t.view(self._tdtype(self.state_dtype)).view(self.num_slots, self.H_v, self.d, self.d)
 
     def nlog_tensor(self):
-        return self.bufs["nlog"][: self.sizes[4]].view(self._torch.int32).view(self.num_slots, self.H_v)
+        return self.bufs["nlog"][: self.sizes[4]].view(self._torch.int32).view(
+            self.num_slots, self.H_v * self.tiles)
 
     # -- calls ------------------------------------------------------------
     def assign(self, slot_ids, init=None) -> None:
@@ -221,7 +233,7 @@ class DeltaLogPool:
         return dl_schedule(self.handle, slot_ids)
 
     def device_log_len(self) -> np.ndarray:
-        return dl_read_log_len_device(self.handle, self.num_slots, self.H_v, self._stream())
+        return dl_read_log_len_device(self.handle, self.num_slots, self.H_v, self._stream(), self.tiles)
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -29,14 +29,15 @@ BUF_NAMES = ("base", "klog", "ulog", "lamlog", "nlog")
 
 EXPORTED = ("dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
             "dl_decode_step", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
-            "dl_schedule", "dl_read_log_len_device", "dl_last_error", "dl_launch_slot_limit")
+            "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error",
+            "dl_launch_slot_limit")
 
 
 class dl_pool_desc(ctypes.Structure):
     _fields_ = [("num_slots", c_int32), ("max_batch", c_int32), ("num_v_heads", c_int32),
                 ("num_k_heads", c_int32), ("d_k", c_int32), ("d_v", c_int32),
                 ("merge_interval", c_int32), ("decay", c_int32), ("update", c_int32),
-                ("state_dtype", c_int32), ("in_dtype", c_int32)]
+                ("state_dtype", c_int32), ("in_dtype", c_int32), ("value_tile", c_int32)]
 
 
 class dl_pool_buffers(ctypes.Structure):
@@ -61,6 +62,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"DeltaLog HIP library not found at {LIB_PATH}; build it with "
                            "`python -m linear_attention_recurrent_dl_amd.build`")
+    # PyTorch ships its own HIP runtime under the same soname; load it first when
+    # it is installed so that the library, torch's allocator and torch's streams
+    # share one runtime whatever the import order of the caller.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     i32p = POINTER(c_int32)
     sig = {
@@ -77,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "dl_get_log_len": (c_int, [c_void_p, i32p]),
         "dl_schedule": (c_int, [c_void_p, c_int32, i32p, i32p, i32p]),
         "dl_read_log_len_device": (c_int, [c_void_p, i32p, c_void_p]),
+        "dl_value_tile": (c_int, [POINTER(dl_pool_desc)]),
         "dl_last_error": (c_char_p, []),
         "dl_launch_slot_limit": (c_int32, []),
     }

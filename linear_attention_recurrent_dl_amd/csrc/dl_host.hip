@@ -19,11 +19,11 @@
 #include <string>
 #include <vector>
 
-#include "../../include/deltalog.h"
+#include "deltalog.h"
 #include "dl_internal.hpp"
 
 namespace dl {
-template <int D>
+template <int D, int BV>
 hipError_t launch_step_d(int, int, int, int, int, const StepParams &, size_t, hipStream_t);
 }
 
@@ -50,6 +50,11 @@ size_t dtype_size(int dt) { return dt == DL_BF16 ? 2 : 4; }
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+int value_tile_of(const dl_pool_desc *d) {
+    return d->value_tile ? d->value_tile
+                         : dl::default_value_tile(d->d_k, d->state_dtype, (long long)d->max_batch * d->num_v_heads);
+}
+
 int validate_desc(const dl_pool_desc *d) {
     if (!d) return fail(DL_ERR_INVALID_ARG, "desc is NULL");
     if (d->num_slots < 1) return fail(DL_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", d->num_slots);
@@ -69,9 +74,12 @@ int validate_desc(const dl_pool_desc *d) {
     if (d->d_k != d->d_v || !supported_dim(d->d_k))
         return fail(DL_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d not built (need d_k == d_v in {16,32,64,128})",
                     d->d_k, d->d_v);
-    if (dl::log_stage_bytes(d->d_k, d->merge_interval - 1, d->decay) > dl::kMaxLogStageBytes)
+    if (d->value_tile != 0 && !dl::value_tile_supported(d->d_k, d->value_tile))
+        return fail(DL_ERR_UNSUPPORTED, "value_tile %d not built for d=%d", d->value_tile, d->d_k);
+    const int bv = value_tile_of(d);
+    if (dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay) > dl::kMaxLogStageBytes)
         return fail(DL_ERR_UNSUPPORTED, "merge_interval %d with d=%d needs %zu B of LDS for the live log (limit %zu)",
-                    d->merge_interval, d->d_k, dl::log_stage_bytes(d->d_k, d->merge_interval - 1, d->decay),
+                    d->merge_interval, d->d_k, dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay),
                     dl::kMaxLogStageBytes);
     const long long units = (long long)d->max_batch * d->num_v_heads;
     if (units > (1LL << 30)) return fail(DL_ERR_INVALID_ARG, "max_batch * num_v_heads too large");
@@ -87,7 +95,7 @@ void compute_sizes(const dl_pool_desc *d, size_t out[DL_NUM_BUFS]) {
     out[DL_BUF_KLOG] = P * Hk * C * D * dtype_size(d->in_dtype);
     out[DL_BUF_ULOG] = P * Hv * C * D * b_size;
     out[DL_BUF_LAMLOG] = d->decay == DL_DECAY_NONE ? 0 : P * Hv * C * lam_w * 4;
-    out[DL_BUF_NLOG] = P * Hv * 4;
+    out[DL_BUF_NLOG] = P * Hv * (D / value_tile_of(d)) * 4;
 }
 
 __global__ void dl_zero_i32_kernel(int32_t *p, size_t n) {
@@ -108,7 +116,7 @@ __global__ void __launch_bounds__(256) dl_assign_kernel(const dl::AssignParams p
     } else {
         for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = make_uint4(0, 0, 0, 0);
     }
-    if (threadIdx.x == 0) p.nlog[sh] = 0;
+    if (threadIdx.x < (unsigned)p.NV) p.nlog[sh * p.NV + threadIdx.x] = 0;
 }
 
 }  // namespace
@@ -120,15 +128,14 @@ int block_threads(int D, int st) {
     return D >= 128 ? 256 : (D >= 64 ? 128 : 64);
 }
 
-int launch_step(int D, int mode, int decay, int update, int st, int it, const StepParams &p, size_t shmem,
+int launch_step(int D, int BV, int mode, int decay, int update, int st, int it, const StepParams &p, size_t shmem,
                 hipStream_t s) {
-    switch (D) {
-    case 16: return (int)launch_step_d<16>(mode, decay, update, st, it, p, shmem, s);
-    case 32: return (int)launch_step_d<32>(mode, decay, update, st, it, p, shmem, s);
-    case 64: return (int)launch_step_d<64>(mode, decay, update, st, it, p, shmem, s);
-    case 128: return (int)launch_step_d<128>(mode, decay, update, st, it, p, shmem, s);
-    default: return (int)hipErrorInvalidValue;
-    }
+#define DL_TILE(d_, bv_) \
+    if (D == d_ && BV == bv_) return (int)launch_step_d<d_, bv_>(mode, decay, update, st, it, p, shmem, s);
+    DL_TILE(128, 128) DL_TILE(128, 64) DL_TILE(128, 32) DL_TILE(128, 16)
+    DL_TILE(64, 64) DL_TILE(64, 32) DL_TILE(32, 32) DL_TILE(16, 16)
+#undef DL_TILE
+    return (int)hipErrorInvalidValue;
 }
 
 int launch_assign(const AssignParams &p, hipStream_t s) {
@@ -141,6 +148,8 @@ int launch_assign(const AssignParams &p, hipStream_t s) {
 struct dl_pool {
     dl_pool_desc desc;
     dl_pool_buffers buf;
+    int bv;                         // value-tile width B_V
+    int nv;                         // value tiles per slot-head
     bool dry;                       // host-only pool: validate + mirror, no device work
     std::vector<int32_t> n;         // host mirror of live-log length per slot
     std::vector<uint32_t> seen;     // duplicate detection (generation stamps)
@@ -195,7 +204,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const int mode = C == 0 ? dl::MODE_EAGER : dl::MODE_STEP;
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, C, d.decay);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay);
         dl::StepParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -214,10 +223,10 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             p.lam = lambda ? lambda + (size_t)lo * Hv * lam_w : nullptr;
             p.beta = beta ? beta + (size_t)lo * Hv : nullptr;
             p.out = out + (size_t)lo * Hv * D;
-            p.nunits = cnt * d.num_v_heads;
+            p.nunits = cnt * d.num_v_heads * pool->nv;
             memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
-            const int e = dl::launch_step(d.d_k, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p, shmem,
-                                          (hipStream_t)stream);
+            const int e = dl::launch_step(d.d_k, pool->bv, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p,
+                                          shmem, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail((hipError_t)e, "decode kernel launch");
         }
     }
@@ -258,6 +267,8 @@ int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_
     dl_pool *p = new (std::nothrow) dl_pool;
     if (!p) return fail(DL_ERR_INVALID_ARG, "out of host memory");
     p->desc = *desc;
+    p->bv = value_tile_of(desc);
+    p->nv = desc->d_k / p->bv;
     p->dry = buffers == nullptr;
     if (buffers) p->buf = *buffers;
     else memset(&p->buf, 0, sizeof p->buf);
@@ -298,6 +309,7 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids, const void
         p.nlog = pool->buf.nlog;
         p.head_bytes = (int64_t)d.d_k * d.d_v * dtype_size(d.state_dtype);
         p.H_v = d.num_v_heads;
+        p.NV = pool->nv;
         for (int32_t lo = 0; lo < n; lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, n - lo);
             p.init = init_base ? static_cast<const char *>(init_base) + (size_t)lo * d.num_v_heads * p.head_bytes
@@ -344,13 +356,13 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, C, d.decay);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay);
         for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);
-            p.nunits = cnt * d.num_v_heads;
+            p.nunits = cnt * d.num_v_heads * pool->nv;
             memcpy(p.slots, live.data() + lo, cnt * sizeof(int32_t));
-            const int e = dl::launch_step(d.d_k, dl::MODE_MERGE, d.decay, d.update, d.state_dtype, d.in_dtype, p,
-                                          shmem, (hipStream_t)stream);
+            const int e = dl::launch_step(d.d_k, pool->bv, dl::MODE_MERGE, d.decay, d.update, d.state_dtype,
+                                          d.in_dtype, p, shmem, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail((hipError_t)e, "merge kernel launch");
         }
     }
@@ -394,11 +406,18 @@ int dl_schedule(const dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t
 int dl_read_log_len_device(dl_pool *pool, int32_t *n_out, void *stream) {
     if (!pool || !n_out) return fail(DL_ERR_INVALID_ARG, "NULL argument");
     if (pool->dry) return fail(DL_ERR_DRY_RUN, "host-only pool has no device counters");
-    const size_t bytes = (size_t)pool->desc.num_slots * pool->desc.num_v_heads * sizeof(int32_t);
+    const size_t bytes = (size_t)pool->desc.num_slots * pool->desc.num_v_heads * pool->nv * sizeof(int32_t);
     hipError_t e = hipMemcpyAsync(n_out, pool->buf.nlog, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "reading log lengths");
     return ok();
+}
+
+int dl_value_tile(const dl_pool_desc *desc) {
+    int rc = validate_desc(desc);
+    if (rc) return rc;
+    g_err.clear();
+    return value_tile_of(desc);
 }
 
 const char *dl_last_error(void) { return g_err.c_str(); }

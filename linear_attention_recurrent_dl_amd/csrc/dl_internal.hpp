@@ -31,7 +31,7 @@ struct StepParams {
     void *klog;          // [P, H_k, C, D]       input dtype
     void *ulog;          // [P, H_v, C, D]       fp32 (delta) | input dtype (plain)
     float *lamlog;       // [P, H_v, C] | [P, H_v, C, D]
-    int32_t *nlog;       // [P, H_v]
+    int32_t *nlog;       // [P, H_v, NV] live length per value tile
     const void *q;       // [n, H_k, D]
     const void *k;       // [n, H_k, D]
     const void *v;       // [n, H_v, D]
@@ -41,34 +41,55 @@ struct StepParams {
     int32_t H_v;
     int32_t H_k;
     int32_t C;           // log capacity L - 1
-    int32_t nunits;      // blocks in this launch = n * H_v
+    int32_t nunits;      // blocks in this launch = n * H_v * (d_v / B_V)
     int32_t slots[kMaxLaunchSlots];
 };
 
 // Arguments of the slot-assignment (fresh base, empty log) kernel.
 struct AssignParams {
     void *base;          // [P, H_v, D, D]
-    int32_t *nlog;       // [P, H_v]
+    int32_t *nlog;       // [P, H_v, NV]
     const void *init;    // [n, H_v, D, D] or NULL (zero state)
     int64_t head_bytes;  // D * D * sizeof(state)
     int32_t H_v;
+    int32_t NV;          // value tiles per slot-head (live-length counters per slot-head)
     int32_t nunits;      // n * H_v
     int32_t slots[kMaxLaunchSlots];
 };
 
 // Dynamic LDS of a decode / merge block: the live log staged as fp32 -- key
-// factors [C][D], value factors [C][D] and, for per-key decay, the snapshots
-// [C][D].  Pools whose log would need more than kMaxLogStageBytes are refused.
+// factors [C][D], value factors on the block's tile [C][BV] and, for per-key
+// decay, the snapshots [C][D].  Pools whose log would need more than
+// kMaxLogStageBytes are refused.
 constexpr size_t kMaxLogStageBytes = 56 * 1024;
-inline size_t log_stage_bytes(int D, int C, int decay) {
-    return (size_t)C * D * sizeof(float) * (decay == DECAY_PER_KEY ? 3 : 2);
+inline size_t log_stage_bytes(int D, int BV, int C, int decay) {
+    return (size_t)C * sizeof(float) * (D + BV + (decay == DECAY_PER_KEY ? D : 0));
+}
+
+// Default value-tile width.  Wide tiles (half the row for an fp32 d = 128
+// state, the whole row otherwise) stream best once a batch fills the GPU with
+// blocks; when max_batch * H_v slot-heads would give fewer blocks than the
+// 256 CUs, 32-column tiles spread one step over more CUs instead.
+inline int default_value_tile(int D, int state_dtype, long long units) {
+    const int wide = (D == 128 && state_dtype != BF16) ? 64 : D;
+    if (D >= 64 && units * (D / wide) < 256) return 32;
+    return wide;
+}
+inline bool value_tile_supported(int D, int BV) {
+    switch (D) {
+    case 128: return BV == 128 || BV == 64 || BV == 32 || BV == 16;
+    case 64: return BV == 64 || BV == 32;
+    case 32: return BV == 32;
+    case 16: return BV == 16;
+    default: return false;
+    }
 }
 
 // Threads per block of the decode kernels for a head dim and state dtype.
 int block_threads(int D, int state_dtype);
 
 // Launch one decode / eager / merge kernel; returns hipError_t as int.
-int launch_step(int D, int mode, int decay, int update, int state_dtype, int in_dtype,
+int launch_step(int D, int BV, int mode, int decay, int update, int state_dtype, int in_dtype,
                 const StepParams &p, size_t shmem, hipStream_t stream);
 
 int launch_assign(const AssignParams &p, hipStream_t stream);

@@ -7,10 +7,13 @@
 // Accelerator for Memory-Bound Linear Attention Decode on FPGA" -- grouped
 // value heads.
 //
-// One block owns one (slot, v-head) pair and the whole d_k x d_v tile, so the
-// paper's ReplayPrep (key-side replay coefficients) and Finalize (commit the
-// log length once) fuse into the block with no scratch buffer and no second
-// launch.  Per block:
+// One block owns the d_k x B_V value tile of one (slot, v-head) pair.  Every
+// block of a slot-head computes the (cheap) key-side replay coefficients
+// itself -- the paper's ReplayPrep -- and owns its own live-length counter,
+// so nothing is shared between blocks within a launch except the key entry
+// and decay snapshot, which only the first tile writes (the paper's
+// designated writer; Finalize becomes each block's own counter write).  No
+// scratch buffer and no second launch.  Per block:
 //
 //   1. issue the base-tile loads: every thread holds RPT rows x VEC columns as
 //      16-byte vectors; for a fixed row index the block reads NT x 16
@@ -133,11 +136,15 @@ __device__ __forceinline__ uint4 pack_16(const float (&x)[N]) {
     return make_uint4(ws[0], ws[1], ws[2], ws[3]);
 }
 
-// Row access of a tile: uniform byte base plus a 32-bit per-lane byte offset,
-// so a thread's RPT loads and stores use one offset register (scalar-base
-// addressing) instead of one 64-bit address per row.
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
+// Row access of a tile: byte base plus a 32-bit per-lane byte offset.  The
+// base tile is read once per step and not again until the next step, so its
+// loads carry the non-temporal (streaming) hint: they do not displace the
+// live log and token data from the caches.
 __device__ __forceinline__ uint4 ld16(const void *base, uint32_t off) {
-    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + off);
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+        reinterpret_cast<const v4u32 *>(static_cast<const char *>(base) + off)));
 }
 
 __device__ __forceinline__ void st16(void *base, uint32_t off, const uint4 &v) {
@@ -151,19 +158,20 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber them so that
-// each XCD works on a contiguous range of (entry, head) units: the v-heads of
-// one q/k group (which share the key-log entries and q/k) then meet in the
-// same L2.
+// each XCD works on a contiguous range of units: the value tiles and v-heads
+// of one q/k group (which share the key-log entries and q / k) then meet in
+// the same L2.
 __device__ __forceinline__ int xcd_unit(int bid, int nb) {
     if ((nb & 7) != 0) return bid;
     return (bid & 7) * (nb >> 3) + (bid >> 3);
 }
 
-// Block geometry for a D x D tile of state type ST.
-template <int D, typename ST>
+// Block geometry: a block owns the D x BV value tile of one (slot, v-head)
+// ([DL] GPU-execution section: work units own d_k x B_V tiles, N_V = d_v / B_V).
+template <int D, int BV, typename ST>
 struct Tile {
     static constexpr int VEC = 16 / (int)sizeof(ST);       // elements per 16-byte load
-    static constexpr int CG = D / VEC;                     // column groups per row
+    static constexpr int CG = BV / VEC;                    // column groups per tile row
     static constexpr int NT = D >= 128 ? 256 : (D >= 64 ? 128 : 64);
     static constexpr int RG = NT / CG;                     // row groups
     static constexpr int RPT = (D + RG - 1) / RG;          // rows per thread
@@ -171,8 +179,9 @@ struct Tile {
     static constexpr bool RAGGED = RG > D;                 // some row groups own no row
     static constexpr int TPE = D / 4;                      // threads per log entry (4 keys each)
     static constexpr int EPP = NT / TPE;                   // log entries per coefficient pass
-    static constexpr int PF = D >= 128 ? 4 : 8;            // log chunks per thread loaded up front
-    static_assert(D % VEC == 0 && NT % CG == 0 && CG <= 64 && TPE <= 64, "tile geometry");
+    static constexpr int PF = RPT >= 16 ? 4 : 8;           // log chunks per thread loaded up front
+    static_assert(BV % VEC == 0 && D % BV == 0 && NT % CG == 0 && CG <= 64 && TPE <= 64 && NT >= D,
+                  "tile geometry");
 };
 
 template <typename T, int N>
@@ -184,19 +193,22 @@ __device__ __forceinline__ void store_lds(float *dst, const uint4 &w) {
         *reinterpret_cast<float4 *>(dst + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
 }
 
-template <int D, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
-__global__ void __launch_bounds__((Tile<D, ST>::NT))
+template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
+__global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
 dl_step_kernel(const StepParams p) {
-    using G = Tile<D, ST>;
+    using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
     constexpr int TPE = G::TPE, EPP = G::EPP, PF = G::PF;
+    constexpr int NV = D / BV;                    // value tiles per slot-head
     constexpr int KV = 16 / (int)sizeof(IT);      // key-factor elements per 16-byte chunk
     constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte chunk
+    constexpr int UCH = BV / UV;                  // value-factor chunks per entry and tile
     constexpr bool TOKEN = MODE != MODE_MERGE;
     constexpr bool LOG = MODE != MODE_EAGER;
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+    static_assert(BV % UV == 0, "value-factor chunks");
 
     __shared__ float s_q[D];        // e^{l'} * q
     __shared__ float s_k[D];        // e^{l'} * k
@@ -204,11 +216,11 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_a[D];        // a (= k for delta)
     __shared__ float s_g[D];        // e^{l'}
     __shared__ float s_lp[D];       // l'
-    __shared__ float s_b[D];        // b (merge broadcast)
+    __shared__ float s_b[BV];       // b on this tile's columns (merge broadcast)
     __shared__ float s_cq[kMaxLogCap + 1];
     __shared__ float s_ck[kMaxLogCap + 1];
     __shared__ float s_lam[kMaxLogCap + 1];   // scalar snapshots
-    __shared__ float s_red[NW][2][D];
+    __shared__ float s_red[NW][2][BV];
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
 
@@ -216,19 +228,22 @@ dl_step_kernel(const StepParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int unit = xcd_unit(blockIdx.x, gridDim.x);
     const int H_v = p.H_v, C = p.C;
-    const int e = unit / H_v, h = unit - e * H_v;
+    const int eh = unit / NV, vt = unit - eh * NV;      // (entry, v-head), value tile
+    const int e = eh / H_v, h = eh - e * H_v;
+    const int c0 = vt * BV;                             // first column of the tile
     const int grp = H_v / p.H_k, g = h / grp;
     const int slot = p.slots[e];
     const size_t sh = (size_t)slot * H_v + h;           // slot-head index
     const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
     const int cg = tid % CG, rg = tid / CG;
+    const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
     float *s_lk = reinterpret_cast<float *>(s_dyn);     // [C][D]: K_i, then e^{l'-Lam_i} * K_i
-    float *s_lu = s_lk + C * D;                         // [C][D]: U_i
-    float *s_ll = s_lu + C * D;                         // [C][D]: Lam_i (per key)
+    float *s_lu = s_lk + C * D;                         // [C][BV]: U_i on this tile's columns
+    float *s_ll = s_lu + C * BV;                        // [C][D]: Lam_i (per key)
 
     int n = 0;
-    if constexpr (LOG) n = p.nlog[sh];
+    if constexpr (LOG) n = p.nlog[sh * NV + vt];
     if constexpr (MODE == MODE_MERGE) {
         if (n == 0) return;                             // empty log: nothing to materialize
     }
@@ -248,7 +263,7 @@ dl_step_kernel(const StepParams p) {
             qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
             kraw = reinterpret_cast<const IT *>(p.k)[qo];
             kv = to_f32(kraw);
-            vv = to_f32(reinterpret_cast<const IT *>(p.v)[((size_t)e * H_v + h) * D + tid]);
+            if (tid < BV) vv = to_f32(reinterpret_cast<const IT *>(p.v)[((size_t)e * H_v + h) * D + c0 + tid]);
             if constexpr (SCALAR) lam = p.lam[(size_t)e * H_v + h];
             if constexpr (PERKEY) lam = p.lam[((size_t)e * H_v + h) * D + tid];
             if constexpr (DELTA) beta = p.beta[(size_t)e * H_v + h];
@@ -261,17 +276,22 @@ dl_step_kernel(const StepParams p) {
     if constexpr (SCALAR && LOG) {
         if (tid < n) lam_i = lamlog[sh * C + tid];
     }
-    // live log as 16-byte chunks: K entries (of the shared q/k head), U entries,
-    // per-key snapshots; each region is contiguous for entries 0 .. n-1
+    // live log as 16-byte chunks: K entries of the shared q/k head (all D keys),
+    // U entries on this tile's columns, per-key snapshots (all D keys)
     const int cK = LOG ? n * D / KV : 0;
-    const int cU = LOG ? n * D / UV : 0;
+    const int cU = LOG ? n * UCH : 0;
     const int cL = (LOG && PERKEY) ? n * D / 4 : 0;
     const int ctot = cK + cU + cL;
     const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gk * C * D);
-    const uint4 *ub = reinterpret_cast<const uint4 *>(ulog + sh * C * D);
+    const BT *ub = ulog + sh * C * D + c0;
     const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + sh * C * D);
     auto chunk_ptr = [&](int x) -> const uint4 * {
-        return x < cK ? kb + x : (x < cK + cU ? ub + (x - cK) : lb + (x - cK - cU));
+        if (x < cK) return kb + x;
+        if (x < cK + cU) {
+            const int u = x - cK, i = u / UCH;
+            return reinterpret_cast<const uint4 *>(ub + (size_t)i * D + (u - i * UCH) * UV);
+        }
+        return lb + (x - cK - cU);
     };
     auto stage = [&](int x, const uint4 &w) {
         if (x < cK) store_lds<IT, KV>(s_lk + x * KV, w);
@@ -286,8 +306,9 @@ dl_step_kernel(const StepParams p) {
             if (x < ctot) pf[m] = *chunk_ptr(x);
         }
     }
-    // base tile of this slot-head; a thread reads rows rg + RG * j
-    const ST *tbase = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D);
+    // base tile, issued after the log so that the coefficient phase below
+    // overlaps its arrival: a thread reads rows rg + RG * j, columns c0 + cg * VEC ..
+    const ST *tbase = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D) + c0;
     const uint32_t toff = (uint32_t)((rg * D + cg * VEC) * sizeof(ST));
     constexpr uint32_t TROW = RG * D * sizeof(ST);      // bytes between a thread's rows
     uint4 tile[RPT];
@@ -381,7 +402,7 @@ dl_step_kernel(const StepParams p) {
         if constexpr (LOG) {
             for (int i = rg; i < n; i += RG) {             // log entries as extra rows
                 const float cq = s_cq[i], ck = s_ck[i];
-                const float *u = s_lu + i * D + cg * VEC;
+                const float *u = s_lu + i * BV + cg * VEC;
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) {
                     accq[c] += cq * u[c];
@@ -421,7 +442,7 @@ dl_step_kernel(const StepParams p) {
         }
         __syncthreads();
 
-        if (tid < D) {
+        if (tid < BV) {
             float yq = 0.f, yk = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
@@ -431,13 +452,19 @@ dl_step_kernel(const StepParams p) {
             float b;
             if constexpr (DELTA) b = beta * (vv - yk);
             else b = vv;
-            p.out[((size_t)e * H_v + h) * D + tid] = yq + s_s * b;
+            p.out[((size_t)e * H_v + h) * D + c0 + tid] = yq + s_s * b;
             if (merge) {
                 s_b[tid] = b;
             } else if constexpr (LOG) {
                 BT *ulw = reinterpret_cast<BT *>(p.ulog);
-                ulw[(sh * C + n) * D + tid] = from_f32<BT>(b);
-                if (h % grp == 0) {                        // designated writer of the key entry
+                ulw[(sh * C + n) * D + c0 + tid] = from_f32<BT>(b);
+            }
+        }
+        if constexpr (LOG) {
+            // the tile-shared entries of the appended token: key factor (first
+            // v-head of the q/k group, first tile) and the decay snapshot
+            if (!merge && owner && tid < D) {
+                if (h % grp == 0) {
                     IT *klw = reinterpret_cast<IT *>(p.klog);
                     klw[(gk * C + n) * D + tid] = kraw;
                 }
@@ -449,11 +476,11 @@ dl_step_kernel(const StepParams p) {
         }
     }
     if constexpr (LOG) {
-        if (tid == 0) p.nlog[sh] = merge ? 0 : n + 1;
+        if (tid == 0) p.nlog[sh * NV + vt] = merge ? 0 : n + 1;
     }
     if (!merge) return;
 
-    // ---- merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T, from registers
+    // ---- merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T on this tile, from registers
     __syncthreads();
     float acc[RPT][VEC];
     float bcol[VEC];
@@ -474,7 +501,7 @@ dl_step_kernel(const StepParams p) {
             float u[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; c += 4) {
-                const float4 u4 = *reinterpret_cast<const float4 *>(s_lu + i * D + cg * VEC + c);
+                const float4 u4 = *reinterpret_cast<const float4 *>(s_lu + i * BV + cg * VEC + c);
                 u[c] = u4.x;
                 u[c + 1] = u4.y;
                 u[c + 2] = u4.z;
@@ -496,19 +523,19 @@ dl_step_kernel(const StepParams p) {
     }
 }
 
-template <int D, int DECAY, bool DELTA, typename ST, typename IT>
+template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT>
 static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipStream_t s) {
-    constexpr int NT = Tile<D, ST>::NT;
+    constexpr int NT = Tile<D, BV, ST>::NT;
     const dim3 grid(p.nunits), block(NT);
     switch (mode) {
     case MODE_STEP:
-        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p);
         break;
     case MODE_EAGER:
-        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p);
         break;
     case MODE_MERGE:
-        dl_step_kernel<D, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p);
         break;
     default:
         return hipErrorInvalidValue;
@@ -516,29 +543,29 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     return hipGetLastError();
 }
 
-template <int D, int DECAY, bool DELTA>
+template <int D, int BV, int DECAY, bool DELTA>
 static hipError_t launch_dtypes(int mode, int st, int it, const StepParams &p, size_t shmem, hipStream_t s) {
-    if (st == F32 && it == F32) return launch_combo<D, DECAY, DELTA, float, float>(mode, p, shmem, s);
-    if (st == F32 && it == BF16) return launch_combo<D, DECAY, DELTA, float, bf16_t>(mode, p, shmem, s);
-    if (st == BF16 && it == F32) return launch_combo<D, DECAY, DELTA, bf16_t, float>(mode, p, shmem, s);
-    if (st == BF16 && it == BF16) return launch_combo<D, DECAY, DELTA, bf16_t, bf16_t>(mode, p, shmem, s);
+    if (st == F32 && it == F32) return launch_combo<D, BV, DECAY, DELTA, float, float>(mode, p, shmem, s);
+    if (st == F32 && it == BF16) return launch_combo<D, BV, DECAY, DELTA, float, bf16_t>(mode, p, shmem, s);
+    if (st == BF16 && it == F32) return launch_combo<D, BV, DECAY, DELTA, bf16_t, float>(mode, p, shmem, s);
+    if (st == BF16 && it == BF16) return launch_combo<D, BV, DECAY, DELTA, bf16_t, bf16_t>(mode, p, shmem, s);
     return hipErrorInvalidValue;
 }
 
-template <int D>
+template <int D, int BV>
 hipError_t launch_step_d(int mode, int decay, int update, int st, int it, const StepParams &p,
                          size_t shmem, hipStream_t s) {
     const bool delta = update != 0;
     switch (decay) {
     case DECAY_NONE:
-        return delta ? launch_dtypes<D, DECAY_NONE, true>(mode, st, it, p, shmem, s)
-                     : launch_dtypes<D, DECAY_NONE, false>(mode, st, it, p, shmem, s);
+        return delta ? launch_dtypes<D, BV, DECAY_NONE, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, BV, DECAY_NONE, false>(mode, st, it, p, shmem, s);
     case DECAY_SCALAR:
-        return delta ? launch_dtypes<D, DECAY_SCALAR, true>(mode, st, it, p, shmem, s)
-                     : launch_dtypes<D, DECAY_SCALAR, false>(mode, st, it, p, shmem, s);
+        return delta ? launch_dtypes<D, BV, DECAY_SCALAR, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, BV, DECAY_SCALAR, false>(mode, st, it, p, shmem, s);
     case DECAY_PER_KEY:
-        return delta ? launch_dtypes<D, DECAY_PER_KEY, true>(mode, st, it, p, shmem, s)
-                     : launch_dtypes<D, DECAY_PER_KEY, false>(mode, st, it, p, shmem, s);
+        return delta ? launch_dtypes<D, BV, DECAY_PER_KEY, true>(mode, st, it, p, shmem, s)
+                     : launch_dtypes<D, BV, DECAY_PER_KEY, false>(mode, st, it, p, shmem, s);
     default:
         return hipErrorInvalidValue;
     }

@@ -1,0 +1,6 @@
+// Decode / eager / merge kernel instantiations for d_k = d_v = 64, value tiles of 64 columns.
+#include "dl_kernels.hpp"
+
+namespace dl {
+template hipError_t launch_step_d<64, 64>(int, int, int, int, int, const StepParams &, size_t, hipStream_t);
+}  // namespace dl

@@ -56,8 +56,25 @@ def test_pool_sizes_formula():
         s_in = 2 if cfg.in_dtype == "bf16" else 4
         s_b = 4 if cfg.update == "delta" else s_in
         lam_w = {"none": 0, "scalar": 1, "per_key": D}[cfg.decay]
+        bv = dl.dl_value_tile(desc)
+        wide = 64 if (D == 128 and cfg.state_dtype == "f32") else D
+        assert bv == (32 if (D >= 64 and cfg.batch * Hv * (D // wide) < 256) else wide), cfg.name
         assert sz == [P * Hv * D * D * s_st, P * Hk * C * D * s_in, P * Hv * C * D * s_b,
-                      P * Hv * C * lam_w * 4, P * Hv * 4], cfg.name
+                      P * Hv * C * lam_w * 4, P * Hv * (D // bv) * 4], cfg.name
+
+
+@pytest.mark.parametrize("d,bv,ok", [(128, 128, True), (128, 64, True), (128, 32, True), (128, 16, True),
+                                     (128, 8, False), (128, 48, False), (64, 64, True), (64, 32, True),
+                                     (64, 16, False), (32, 32, True), (32, 16, False), (16, 16, True)])
+def test_value_tile_choices(d, bv, ok):
+    desc = dl.make_desc(4, 4, 2, 2, d, 4, "scalar", "delta", "f32", "f32", value_tile=bv)
+    if ok:
+        assert dl.dl_value_tile(desc) == bv
+        assert dl.dl_pool_sizes(desc)[4] == 4 * 2 * (d // bv) * 4
+    else:
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_value_tile(desc)
+        assert ei.value.code == N.DL_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("field,value,code", [

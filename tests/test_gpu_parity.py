@@ -123,3 +123,28 @@ def test_batch_split_across_launches():
     cfg = small_variant(CONFIGS[1], batch=lim + 37, steps=10, L=4, d=16, H_v=2, H_k=1,
                         name="split_launch")
     _check(cfg, run(cfg, track=[0, lim - 1, lim, lim + 36]))
+
+
+# ---- every built value-tile width (work units own d_k x B_V tiles)
+TILES = [(128, 128), (128, 64), (128, 32), (128, 16), (64, 64), (64, 32)]
+
+
+@pytest.mark.parametrize("d,bv", TILES)
+@pytest.mark.parametrize("base_idx", [2, 3, 4, 5])
+def test_value_tiles(d, bv, base_idx):
+    from gpu_harness import run
+    base = CONFIGS[base_idx]
+    kw = dict(batch=3, steps=2 * base.L + 5, d=d, H_v=4, H_k=2 if base.H_k < base.H_v else 4,
+              name=f"{base.name}_d{d}_bv{bv}")
+    if base.random_slots:
+        kw.update(num_slots=9, replace_per_step=1)
+    cfg = small_variant(base, **kw)
+    _check(cfg, run(cfg, value_tile=bv, merge_every=7))
+
+
+@pytest.mark.parametrize("bv", [128, 64, 32, 16])
+def test_value_tiles_headline_gdn(bv):
+    """The batch-1 GDN workload at every tile width, every output compared."""
+    from gpu_harness import run
+    cfg = CONFIGS[2]
+    _check(cfg, run(cfg, value_tile=bv))
