@@ -109,7 +109,14 @@ typedef struct {
 
 /* Device buffers of a pool, allocated by the caller with the sizes
  * dl_pool_sizes returns (a size may be 0, then the pointer may be NULL).
- *   base    [P, H_v, d_k, d_v]          state_dtype   dense base S_bar
+ *   base    [P, H_v, d_v / B_V, d_k, B_V]  state_dtype   dense base S_bar, value-tile
+ *                                                     major: each d_k x B_V tile
+ *                                                     (rows = keys) is contiguous;
+ *                                                     the natural [d_k, d_v] layout
+ *                                                     when B_V == d_v.  Callers
+ *                                                     exchange states in the natural
+ *                                                     layout via dl_slot_assign and
+ *                                                     dl_read_base.
  *   klog    [P, H_k, L-1, d_k]          in_dtype      key factors a_i (one per q/k head)
  *   ulog    [P, H_v, L-1, d_v]          fp32 | in     value factors b_i
  *   lamlog  [P, H_v, L-1] (scalar) or [P, H_v, L-1, d_k] (per key)  fp32
@@ -147,10 +154,12 @@ int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_
 int dl_pool_destroy(dl_pool *pool);
 
 /* Allocator ([DL] serving-integration section): give n slots a fresh state.
- *   slot_ids   host int32 [n], distinct, in range
- *   init_base  device [n, H_v, d_k, d_v] in state_dtype, or NULL for a zero state
- * Copies init_base[j] into base[slot_ids[j]] and empties that slot's log; the
- * slot's previous log is discarded, not merged.  Other slots are untouched. */
+ *   slot_ids   host int32 [n], distinct, in range, n <= max_batch
+ *   init_base  device [n, H_v, d_k, d_v] in state_dtype (natural layout), or
+ *              NULL for a zero state
+ * Copies init_base[j] into base[slot_ids[j]] (re-laid out into value tiles)
+ * and empties that slot's log; the slot's previous log is discarded, not
+ * merged.  Other slots are untouched. */
 int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids,
                    const void *init_base, void *stream);
 
@@ -187,6 +196,14 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream);
 
 /* dl_merge over every slot whose log is not empty.  Idempotent. */
 int dl_flush_all(dl_pool *pool, void *stream);
+
+/* Copy the bases of n slots out in the natural layout.
+ *   slot_ids  host int32 [n], distinct, in range, n <= max_batch
+ *   out       device [n, H_v, d_k, d_v] in state_dtype, 16-byte aligned
+ * Enqueued on the stream; the pool is not modified.  A base is the slot's
+ * logical state only when its log is empty: call dl_merge (or dl_flush_all)
+ * first to read logical states.  DL_ERR_DRY_RUN on a host-only pool. */
+int dl_read_base(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *out, void *stream);
 
 /* Host mirror of the live-log length of every slot: n_out host int32 [P]. */
 int dl_get_log_len(const dl_pool *pool, int32_t *n_out);

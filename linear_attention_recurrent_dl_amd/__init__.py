@@ -84,6 +84,11 @@ def dl_flush_all(pool: int, stream) -> None:
     N.check(N.lib().dl_flush_all(pool, stream), "dl_flush_all")
 
 
+def dl_read_base(pool: int, slot_ids, out, stream) -> None:
+    ids = _ids(slot_ids)
+    N.check(N.lib().dl_read_base(pool, len(ids), _i32p(ids), N.ptr(out), stream), "dl_read_base")
+
+
 def dl_get_log_len(pool: int, num_slots: int) -> np.ndarray:
     out = np.zeros(num_slots, dtype=np.int32)
     N.check(N.lib().dl_get_log_len(pool, _i32p(out)), "dl_get_log_len")
@@ -172,10 +177,22 @@ class DeltaLogPool:
             raise ValueError(f"{what}: must be a contiguous CUDA tensor")
 
     @property
-    def base(self):
-        """[P, H_v, d, d] view of the dense base (state dtype)."""
+    def base_tiles(self):
+        """[P, H_v, d / B_V, d, B_V] view of the value-tile-major dense base."""
         t = self.bufs["base"][: self.sizes[0]]
-        return t.view(self._tdtype(self.state_dtype)).view(self.num_slots, self.H_v, self.d, self.d)
+        return t.view(self._tdtype(self.state_dtype)).view(
+            self.num_slots, self.H_v, self.tiles, self.d, self.value_tile)
+
+    def read_base(self, slot_ids) -> "torch.Tensor":
+        """Bases of the given slots in the natural layout, [n, H_v, d, d] (state
+        dtype), in launches of at most max_batch slots.  A base is the logical
+        state only for a slot whose log is empty (after merge / flush_all)."""
+        ids = _ids(slot_ids)
+        out = self._torch.empty((len(ids), self.H_v, self.d, self.d), dtype=self._tdtype(self.state_dtype),
+                                device=self.bufs["base"].device)
+        for lo in range(0, len(ids), self.max_batch):
+            dl_read_base(self.handle, ids[lo: lo + self.max_batch], out[lo: lo + self.max_batch], self._stream())
+        return out
 
     def nlog_tensor(self):
         return self.bufs["nlog"][: self.sizes[4]].view(self._torch.int32).view(

@@ -102,21 +102,26 @@ __global__ void dl_zero_i32_kernel(int32_t *p, size_t n) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// Fresh-slot assignment: one block per (slot, v-head), 16-byte copies of the
-// given base (or zeros), then an empty log.
-__global__ void __launch_bounds__(256) dl_assign_kernel(const dl::AssignParams p) {
+// Whole-slot state copies, one block per (slot, v-head), in 16-byte vectors.
+// Vector i of a slot-head in the pool's tile-major base is (tile vt, row r,
+// vector cv of the tile row); in the natural layout it sits at row r, vector
+// vt * tile_vecs + cv.  Assignment (to_pool) also empties the slot's log.
+__global__ void __launch_bounds__(256) dl_copy_state_kernel(const dl::CopyParams p) {
     const int unit = blockIdx.x;
     const int j = unit / p.H_v, h = unit - j * p.H_v;
     const size_t sh = (size_t)p.slots[j] * p.H_v + h;
-    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(p.base) + sh * p.head_bytes);
-    const int64_t nvec = p.head_bytes / 16;
-    if (p.init) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(p.init) + (size_t)unit * p.head_bytes);
-        for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = src[i];
-    } else {
-        for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) dst[i] = make_uint4(0, 0, 0, 0);
+    const int tv = p.tile_vecs, tile_v = p.D * tv;
+    const int nvec = p.D * p.row_vecs;
+    uint4 *pool = reinterpret_cast<uint4 *>(p.base) + sh * nvec;
+    uint4 *ext = p.ext ? reinterpret_cast<uint4 *>(p.ext) + (size_t)unit * nvec : nullptr;
+    for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+        const int vt = i / tile_v, rem = i - vt * tile_v;
+        const int r = rem / tv, cv = rem - r * tv;
+        const int nat = r * p.row_vecs + vt * tv + cv;
+        if (p.to_pool) pool[i] = ext ? ext[nat] : make_uint4(0, 0, 0, 0);
+        else ext[nat] = pool[i];
     }
-    if (threadIdx.x < (unsigned)p.NV) p.nlog[sh * p.NV + threadIdx.x] = 0;
+    if (p.to_pool && threadIdx.x < (unsigned)p.NV) p.nlog[sh * p.NV + threadIdx.x] = 0;
 }
 
 }  // namespace
@@ -138,8 +143,8 @@ int launch_step(int D, int BV, int mode, int decay, int update, int st, int it, 
     return (int)hipErrorInvalidValue;
 }
 
-int launch_assign(const AssignParams &p, hipStream_t s) {
-    dl_assign_kernel<<<dim3(p.nunits), dim3(256), 0, s>>>(p);
+int launch_copy(const CopyParams &p, hipStream_t s) {
+    dl_copy_state_kernel<<<dim3(p.nunits), dim3(256), 0, s>>>(p);
     return (int)hipGetLastError();
 }
 
@@ -179,6 +184,33 @@ int check_slots(dl_pool *pool, int32_t B, const int32_t *ids) {
 
 int hip_fail(hipError_t e, const char *what) {
     return fail(DL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Natural-layout states in or out of the pool's tile-major base, split into
+// launches of at most kMaxLaunchSlots slots.  ext: [n, H_v, d_k, d_v].
+int copy_states(dl_pool *pool, int32_t n, const int32_t *ids, void *ext, bool to_pool, void *stream) {
+    const dl_pool_desc &d = pool->desc;
+    const size_t esz = dtype_size(d.state_dtype);
+    const size_t head_bytes = (size_t)d.d_k * d.d_v * esz;
+    dl::CopyParams p;
+    memset(&p, 0, sizeof p);
+    p.base = pool->buf.base;
+    p.nlog = pool->buf.nlog;
+    p.to_pool = to_pool ? 1 : 0;
+    p.row_vecs = (int32_t)(d.d_v * esz / 16);
+    p.tile_vecs = (int32_t)(pool->bv * esz / 16);
+    p.D = d.d_k;
+    p.H_v = d.num_v_heads;
+    p.NV = pool->nv;
+    for (int32_t lo = 0; lo < n; lo += dl::kMaxLaunchSlots) {
+        const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, n - lo);
+        p.ext = ext ? static_cast<char *>(ext) + (size_t)lo * d.num_v_heads * head_bytes : nullptr;
+        p.nunits = cnt * d.num_v_heads;
+        memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+        const int e = dl::launch_copy(p, (hipStream_t)stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Shared by dl_decode_step and dl_eager_step.
@@ -302,25 +334,23 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids, const void
     if (init_base && ((uintptr_t)init_base & 15)) return fail(DL_ERR_INVALID_ARG, "init_base is not 16-byte aligned");
     if (n == 0) return ok();
     if (!pool->dry) {
-        const dl_pool_desc &d = pool->desc;
-        dl::AssignParams p;
-        memset(&p, 0, sizeof p);
-        p.base = pool->buf.base;
-        p.nlog = pool->buf.nlog;
-        p.head_bytes = (int64_t)d.d_k * d.d_v * dtype_size(d.state_dtype);
-        p.H_v = d.num_v_heads;
-        p.NV = pool->nv;
-        for (int32_t lo = 0; lo < n; lo += dl::kMaxLaunchSlots) {
-            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, n - lo);
-            p.init = init_base ? static_cast<const char *>(init_base) + (size_t)lo * d.num_v_heads * p.head_bytes
-                               : nullptr;
-            p.nunits = cnt * d.num_v_heads;
-            memcpy(p.slots, slot_ids + lo, cnt * sizeof(int32_t));
-            const int e = dl::launch_assign(p, (hipStream_t)stream);
-            if (e != hipSuccess) return hip_fail((hipError_t)e, "assign kernel launch");
-        }
+        const int e = copy_states(pool, n, slot_ids, const_cast<void *>(init_base), true, stream);
+        if (e != hipSuccess) return hip_fail((hipError_t)e, "assign kernel launch");
     }
     for (int32_t j = 0; j < n; ++j) pool->n[slot_ids[j]] = 0;
+    return ok();
+}
+
+int dl_read_base(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *out, void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_slots(pool, n, slot_ids);
+    if (rc) return rc;
+    if (pool->dry) return fail(DL_ERR_DRY_RUN, "host-only pool has no device state");
+    if (n == 0) return ok();
+    if (!out) return fail(DL_ERR_INVALID_ARG, "out is NULL");
+    if ((uintptr_t)out & 15) return fail(DL_ERR_INVALID_ARG, "out is not 16-byte aligned");
+    const int e = copy_states(pool, n, slot_ids, out, false, stream);
+    if (e != hipSuccess) return hip_fail((hipError_t)e, "read kernel launch");
     return ok();
 }
 

@@ -27,7 +27,7 @@ enum Decay : int { DECAY_NONE = 0, DECAY_SCALAR = 1, DECAY_PER_KEY = 2 };
 // Arguments of the decode / eager / merge kernels.  Token-side pointers are
 // already offset to this launch's first batch entry.
 struct StepParams {
-    void *base;          // [P, H_v, D, D]       state dtype
+    void *base;          // [P, H_v, NV, D, BV]  state dtype, value-tile major
     void *klog;          // [P, H_k, C, D]       input dtype
     void *ulog;          // [P, H_v, C, D]       fp32 (delta) | input dtype (plain)
     float *lamlog;       // [P, H_v, C] | [P, H_v, C, D]
@@ -45,12 +45,17 @@ struct StepParams {
     int32_t slots[kMaxLaunchSlots];
 };
 
-// Arguments of the slot-assignment (fresh base, empty log) kernel.
-struct AssignParams {
-    void *base;          // [P, H_v, D, D]
+// Arguments of the state-copy kernel (slot assignment and base read-back):
+// whole-slot state copies between the caller's natural layout [n, H_v, D, D]
+// and the pool's value-tile-major base [P, H_v, NV, D, BV].
+struct CopyParams {
+    void *base;          // [P, H_v, NV, D, BV]
     int32_t *nlog;       // [P, H_v, NV]
-    const void *init;    // [n, H_v, D, D] or NULL (zero state)
-    int64_t head_bytes;  // D * D * sizeof(state)
+    void *ext;           // [n, H_v, D, D] natural layout; NULL = zero state (to the pool only)
+    int32_t to_pool;     // 1: ext -> base and empty the log (assign); 0: base -> ext (read)
+    int32_t row_vecs;    // 16-byte vectors per natural row (D * sizeof(state) / 16)
+    int32_t tile_vecs;   // 16-byte vectors per tile row (BV * sizeof(state) / 16)
+    int32_t D;
     int32_t H_v;
     int32_t NV;          // value tiles per slot-head (live-length counters per slot-head)
     int32_t nunits;      // n * H_v
@@ -92,6 +97,6 @@ int block_threads(int D, int state_dtype);
 int launch_step(int D, int BV, int mode, int decay, int update, int state_dtype, int in_dtype,
                 const StepParams &p, size_t shmem, hipStream_t stream);
 
-int launch_assign(const AssignParams &p, hipStream_t stream);
+int launch_copy(const CopyParams &p, hipStream_t stream);
 
 }  // namespace dl

@@ -151,10 +151,10 @@ __device__ __forceinline__ void st16(void *base, uint32_t off, const uint4 &v) {
     *reinterpret_cast<uint4 *>(static_cast<char *>(base) + off) = v;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+// Stores of data no block reads again in this launch (the step's output and
+// appended value factor) carry the non-temporal hint as well.
+__device__ __forceinline__ void st16_stream(void *base, uint32_t off, const uint4 &v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(v4u32, v), reinterpret_cast<v4u32 *>(static_cast<char *>(base) + off));
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber them so that
@@ -216,11 +216,12 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_a[D];        // a (= k for delta)
     __shared__ float s_g[D];        // e^{l'}
     __shared__ float s_lp[D];       // l'
-    __shared__ float s_b[BV];       // b on this tile's columns (merge broadcast)
+    __shared__ __align__(16) float s_b[BV];   // b on this tile's columns (merge broadcast)
+    __shared__ __align__(16) float s_v[BV];   // v on this tile's columns
     __shared__ float s_cq[kMaxLogCap + 1];
     __shared__ float s_ck[kMaxLogCap + 1];
     __shared__ float s_lam[kMaxLogCap + 1];   // scalar snapshots
-    __shared__ float s_red[NW][2][BV];
+    __shared__ __align__(16) float s_red[NW][2][BV];
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
 
@@ -307,10 +308,12 @@ dl_step_kernel(const StepParams p) {
         }
     }
     // base tile, issued after the log so that the coefficient phase below
-    // overlaps its arrival: a thread reads rows rg + RG * j, columns c0 + cg * VEC ..
-    const ST *tbase = reinterpret_cast<const ST *>(p.base) + sh * (size_t)(D * D) + c0;
-    const uint32_t toff = (uint32_t)((rg * D + cg * VEC) * sizeof(ST));
-    constexpr uint32_t TROW = RG * D * sizeof(ST);      // bytes between a thread's rows
+    // overlaps its arrival.  The base is value-tile major, [slot-head][NV][D][BV],
+    // so the tile is one contiguous run: a thread reads tile rows rg + RG * j,
+    // columns cg * VEC ..
+    const ST *tbase = reinterpret_cast<const ST *>(p.base) + (sh * NV + vt) * (size_t)(D * BV);
+    const uint32_t toff = (uint32_t)((rg * BV + cg * VEC) * sizeof(ST));
+    constexpr uint32_t TROW = RG * BV * sizeof(ST);     // bytes between a thread's rows
     uint4 tile[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
@@ -329,6 +332,7 @@ dl_step_kernel(const StepParams p) {
             s_a[tid] = kv;
             s_q[tid] = gg * qv;
             s_k[tid] = gg * kv;
+            if (tid < BV) s_v[tid] = vv;
         }
     }
     if constexpr (LOG) {
@@ -440,43 +444,82 @@ dl_step_kernel(const StepParams p) {
                 s_red[wave][1][cg * VEC + c] = acck[c];
             }
         }
-        __syncthreads();
-
-        if (tid < BV) {
-            float yq = 0.f, yk = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                yq += s_red[w][0][tid];
-                yk += s_red[w][1][tid];
-            }
-            float b;
-            if constexpr (DELTA) b = beta * (vv - yk);
-            else b = vv;
-            p.out[((size_t)e * H_v + h) * D + c0 + tid] = yq + s_s * b;
-            if (merge) {
-                s_b[tid] = b;
-            } else if constexpr (LOG) {
-                BT *ulw = reinterpret_cast<BT *>(p.ulog);
-                ulw[(sh * C + n) * D + c0 + tid] = from_f32<BT>(b);
-            }
-        }
+        // stores that need no reduced value go out before the barrier, once
+        // this wave's loads are consumed: the appended token's tile-shared
+        // entries (key factor from the first v-head of the q/k group, decay
+        // snapshot; first tile only) and this block's live-length counter.
+        // No block of this launch reads entry n or another block's counter.
         if constexpr (LOG) {
-            // the tile-shared entries of the appended token: key factor (first
-            // v-head of the q/k group, first tile) and the decay snapshot
             if (!merge && owner && tid < D) {
-                if (h % grp == 0) {
-                    IT *klw = reinterpret_cast<IT *>(p.klog);
-                    klw[(gk * C + n) * D + tid] = kraw;
-                }
+                if (h % grp == 0) reinterpret_cast<IT *>(p.klog)[(gk * C + n) * D + tid] = kraw;
                 if constexpr (PERKEY) p.lamlog[(sh * C + n) * D + tid] = s_lp[tid];
                 if constexpr (SCALAR) {
                     if (tid == 0) p.lamlog[sh * C + n] = s_lp[0];
                 }
             }
+            if (tid == 0) p.nlog[sh * NV + vt] = merge ? 0 : n + 1;
+        }
+        __syncthreads();
+
+        // output and appended value factor leave in one 16-byte store per lane:
+        // NO lanes cover 4 output columns each, then NU lanes one value-factor
+        // chunk (UV columns) each.  Out lanes also publish b for a merge.
+        constexpr int NO = BV / 4;
+        constexpr int NU = LOG ? BV / UV : 0;
+        constexpr int MC = UV > 4 ? UV : 4;
+        static_assert(NO + NU <= 64, "column lanes fit one wave");
+        const bool is_u = tid >= NO;
+        if (tid < NO || (tid < NO + NU && !merge)) {
+            const int cb = is_u ? (tid - NO) * UV : tid * 4;       // first column in the tile
+            const int nc = is_u ? UV : 4;
+            float ov[MC], bc[MC];
+#pragma unroll
+            for (int c4 = 0; c4 < MC; c4 += 4) {
+                if (c4 < nc) {
+                    float4 yq = make_float4(0.f, 0.f, 0.f, 0.f), yk = yq;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&s_red[w][0][cb + c4]);
+                        yq.x += a.x; yq.y += a.y; yq.z += a.z; yq.w += a.w;
+                        if constexpr (DELTA) {
+                            const float4 b4 = *reinterpret_cast<const float4 *>(&s_red[w][1][cb + c4]);
+                            yk.x += b4.x; yk.y += b4.y; yk.z += b4.z; yk.w += b4.w;
+                        }
+                    }
+                    const float4 v4 = *reinterpret_cast<const float4 *>(&s_v[cb + c4]);
+                    const float yqa[4] = {yq.x, yq.y, yq.z, yq.w}, yka[4] = {yk.x, yk.y, yk.z, yk.w};
+                    const float va[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float b = DELTA ? beta * (va[j] - yka[j]) : va[j];
+                        bc[c4 + j] = b;
+                        ov[c4 + j] = yqa[j] + s_s * b;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bc[c4 + j] = ov[c4 + j] = 0.f;
+                }
+            }
+            if (merge && !is_u)
+                *reinterpret_cast<float4 *>(&s_b[cb]) = make_float4(bc[0], bc[1], bc[2], bc[3]);
+            const uint4 wo = make_uint4(__float_as_uint(ov[0]), __float_as_uint(ov[1]),
+                                        __float_as_uint(ov[2]), __float_as_uint(ov[3]));
+            uint4 wu = wo;
+            if constexpr (LOG) {
+                float ub[UV];
+#pragma unroll
+                for (int c = 0; c < UV; ++c) ub[c] = bc[c];
+                wu = pack_16<BT, UV>(ub);
+            }
+            char *dst = is_u ? reinterpret_cast<char *>(p.ulog) + ((sh * C + n) * D + c0 + cb) * sizeof(BT)
+                             : reinterpret_cast<char *>(p.out) + (((size_t)e * H_v + h) * D + c0 + cb) * sizeof(float);
+            // per-component select: a select of whole vectors goes through scratch
+            st16_stream(dst, 0, make_uint4(is_u ? wu.x : wo.x, is_u ? wu.y : wo.y, is_u ? wu.z : wo.z,
+                                    is_u ? wu.w : wo.w));
         }
     }
-    if constexpr (LOG) {
-        if (tid == 0) p.nlog[sh * NV + vt] = merge ? 0 : n + 1;
+    if constexpr (MODE == MODE_MERGE) {
+        if (tid == 0) p.nlog[sh * NV + vt] = 0;
     }
     if (!merge) return;
 

@@ -140,7 +140,7 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
     pool.flush_all()
     torch.cuda.synchronize()
     res.counter_mismatch += int(np.sum(pool.device_log_len() != 0))
-    S_gpu = pool.base[torch.tensor(track, device=DEV)].float().cpu().numpy()
+    S_gpu = pool.read_base(track).float().cpu().numpy()
     st_e = RelL2()
     st_e.add(S_gpu, E.states())
     res.out_err, res.state_err = out_e.value, st_e.value

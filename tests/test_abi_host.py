@@ -161,6 +161,24 @@ def test_token_pointer_rules():
     assert ei.value.code == N.DL_ERR_DRY_RUN
 
 
+def test_read_base_rules():
+    lib = N.lib()
+    p = _host_pool()
+    ids = np.array([0, 1], dtype=np.int32)
+    ip = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    # a host-only pool has no device state to read
+    assert lib.dl_read_base(p.handle, 2, ip, 16, None) == N.DL_ERR_DRY_RUN
+    # slot validation comes first, as for every slot call
+    dup = np.array([1, 1], dtype=np.int32)
+    assert lib.dl_read_base(p.handle, 2, dup.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 16,
+                            None) == N.DL_ERR_DUPLICATE_SLOT
+    big = np.arange(5, dtype=np.int32)
+    assert lib.dl_read_base(p.handle, 5, big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 16,
+                            None) == N.DL_ERR_BATCH_TOO_LARGE
+    assert lib.dl_read_base(None, 2, ip, 16, None) == N.DL_ERR_INVALID_ARG
+    assert p.log_len().tolist() == [0] * 8
+
+
 @pytest.mark.parametrize("L", [1, 2, 5, 16])
 def test_host_schedule_matches_closed_form(L):
     rng = np.random.default_rng(L)
