@@ -4,7 +4,10 @@
 
 Each ``csrc/*.hip`` file is compiled separately (in parallel) with hipcc and
 linked into one shared library next to this file.  Packed-fp32 instructions are
-disabled for all device code (``-packed-fp32-ops``).
+disabled for all device code (``-packed-fp32-ops``).  The compiler's per-kernel
+resource report is read back: a kernel that needs scratch memory (register
+spills, or a private array the compiler could not keep in registers) fails the
+build, since it would stall every block of these bandwidth-bound kernels.
 """
 
 from __future__ import annotations
@@ -12,6 +15,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -42,12 +46,34 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+_FUNC = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def scratch_kernels(report: str) -> list:
+    """(kernel, bytes per lane) of every kernel with scratch in a resource report."""
+    out, name = [], None
+    for line in report.splitlines():
+        m = _FUNC.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str, extra: list) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc()] + compile_flags() + extra + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + compile_flags() + extra + ["-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    bad = scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory: " +
+                           ", ".join(f"{k} ({b} B/lane)" for k, b in bad))
     return obj
 
 

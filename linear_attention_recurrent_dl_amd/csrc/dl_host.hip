@@ -77,9 +77,10 @@ int validate_desc(const dl_pool_desc *d) {
     if (d->value_tile != 0 && !dl::value_tile_supported(d->d_k, d->value_tile))
         return fail(DL_ERR_UNSUPPORTED, "value_tile %d not built for d=%d", d->value_tile, d->d_k);
     const int bv = value_tile_of(d);
-    if (dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay) > dl::kMaxLogStageBytes)
+    if (dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay, d->update, d->in_dtype) > dl::kMaxLogStageBytes)
         return fail(DL_ERR_UNSUPPORTED, "merge_interval %d with d=%d needs %zu B of LDS for the live log (limit %zu)",
-                    d->merge_interval, d->d_k, dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay),
+                    d->merge_interval, d->d_k,
+                    dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay, d->update, d->in_dtype),
                     dl::kMaxLogStageBytes);
     const long long units = (long long)d->max_batch * d->num_v_heads;
     if (units > (1LL << 30)) return fail(DL_ERR_INVALID_ARG, "max_batch * num_v_heads too large");
@@ -236,7 +237,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const int mode = C == 0 ? dl::MODE_EAGER : dl::MODE_STEP;
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
         dl::StepParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -386,7 +387,7 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay);
+        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
         for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);
             p.nunits = cnt * d.num_v_heads * pool->nv;

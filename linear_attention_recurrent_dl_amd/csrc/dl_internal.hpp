@@ -62,13 +62,16 @@ struct CopyParams {
     int32_t slots[kMaxLaunchSlots];
 };
 
-// Dynamic LDS of a decode / merge block: the live log staged as fp32 -- key
-// factors [C][D], value factors on the block's tile [C][BV] and, for per-key
-// decay, the snapshots [C][D].  Pools whose log would need more than
-// kMaxLogStageBytes are refused.
+// Dynamic LDS of a decode / merge block: the live log as stored, back to
+// back -- key factors [n][D] (input type), value factors on the block's tile
+// [n][BV] (fp32 for delta updates, else input type) and, for per-key decay,
+// the snapshots [n][D] (fp32) -- sized for a full log.  Pools whose log would
+// need more than kMaxLogStageBytes are refused.
 constexpr size_t kMaxLogStageBytes = 56 * 1024;
-inline size_t log_stage_bytes(int D, int BV, int C, int decay) {
-    return (size_t)C * sizeof(float) * (D + BV + (decay == DECAY_PER_KEY ? D : 0));
+inline size_t log_stage_bytes(int D, int BV, int C, int decay, int update, int in_dtype) {
+    const size_t s_in = in_dtype == BF16 ? 2 : 4;
+    const size_t s_b = update != 0 ? 4 : s_in;
+    return (size_t)C * (D * s_in + BV * s_b + (decay == DECAY_PER_KEY ? D * sizeof(float) : 0));
 }
 
 // Default value-tile width.  Wide tiles (half the row for an fp32 d = 128

@@ -184,13 +184,25 @@ struct Tile {
                   "tile geometry");
 };
 
+// N consecutive elements of type T from LDS, as fp32 (N a multiple of 4).
 template <typename T, int N>
-__device__ __forceinline__ void store_lds(float *dst, const uint4 &w) {
-    float x[N];
-    unpack_f32<T, N>(w, x);
+__device__ __forceinline__ void lds_f32(const T *src, float (&x)[N]) {
 #pragma unroll
-    for (int c = 0; c < N; c += 4)
-        *reinterpret_cast<float4 *>(dst + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+    for (int c = 0; c < N; c += 4) {
+        if constexpr (sizeof(T) == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + c);
+            x[c] = v.x;
+            x[c + 1] = v.y;
+            x[c + 2] = v.z;
+            x[c + 3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src + c);
+            x[c] = __uint_as_float(v.x << 16);
+            x[c + 1] = __uint_as_float(v.x & 0xffff0000u);
+            x[c + 2] = __uint_as_float(v.y << 16);
+            x[c + 3] = __uint_as_float(v.y & 0xffff0000u);
+        }
+    }
 }
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
@@ -221,6 +233,7 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_cq[kMaxLogCap + 1];
     __shared__ float s_ck[kMaxLogCap + 1];
     __shared__ float s_lam[kMaxLogCap + 1];   // scalar snapshots
+    __shared__ float s_w[kMaxLogCap + 1];     // e^{l' - Lam_i} of a scalar decay (merge)
     __shared__ __align__(16) float s_red[NW][2][BV];
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
@@ -238,10 +251,6 @@ dl_step_kernel(const StepParams p) {
     const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
     const int cg = tid % CG, rg = tid / CG;
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
-
-    float *s_lk = reinterpret_cast<float *>(s_dyn);     // [C][D]: K_i, then e^{l'-Lam_i} * K_i
-    float *s_lu = s_lk + C * D;                         // [C][BV]: U_i on this tile's columns
-    float *s_ll = s_lu + C * BV;                        // [C][D]: Lam_i (per key)
 
     int n = 0;
     if constexpr (LOG) n = p.nlog[sh * NV + vt];
@@ -283,6 +292,13 @@ dl_step_kernel(const StepParams p) {
     const int cU = LOG ? n * UCH : 0;
     const int cL = (LOG && PERKEY) ? n * D / 4 : 0;
     const int ctot = cK + cU + cL;
+    // the live log lands in LDS as stored, chunk x at byte 16 x: key factors
+    // [n][D], value factors on this tile [n][BV], per-key snapshots [n][D]
+    // (overwritten by e^{l'-Lam_i} * K_i for a merge)
+    char *s_log = reinterpret_cast<char *>(s_dyn);
+    const IT *s_lk = reinterpret_cast<const IT *>(s_log);
+    const BT *s_lu = reinterpret_cast<const BT *>(s_log + (size_t)cK * 16);
+    float *s_ll = reinterpret_cast<float *>(s_log + (size_t)(cK + cU) * 16);
     const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gk * C * D);
     const BT *ub = ulog + sh * C * D + c0;
     const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + sh * C * D);
@@ -294,10 +310,10 @@ dl_step_kernel(const StepParams p) {
         }
         return lb + (x - cK - cU);
     };
-    auto stage = [&](int x, const uint4 &w) {
-        if (x < cK) store_lds<IT, KV>(s_lk + x * KV, w);
-        else if (x < cK + cU) store_lds<BT, UV>(s_lu + (x - cK) * UV, w);
-        else store_lds<float, 4>(s_ll + (x - cK - cU) * 4, w);
+    // (stored per component: an aggregate copy out of the prefetch array would
+    // keep that array in scratch memory)
+    auto stage = [&](int x, const uint4 w) {
+        *reinterpret_cast<uint4 *>(s_log + (size_t)x * 16) = make_uint4(w.x, w.y, w.z, w.w);
     };
     uint4 pf[PF];
     if constexpr (LOG) {
@@ -356,19 +372,21 @@ dl_step_kernel(const StepParams p) {
         const int r0 = (tid % TPE) * 4;
         float pq = 0.f, pk = 0.f;
         if (LOG && i < n) {
-            const float4 k4 = *reinterpret_cast<const float4 *>(s_lk + i * D + r0);
-            float kt[4] = {k4.x, k4.y, k4.z, k4.w};
+            float kt[4];
+            lds_f32<IT, 4>(s_lk + i * D + r0, kt);
             if constexpr (PERKEY) {
                 const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + r0);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[r0 + j] - lv[j]);
-            } else if constexpr (SCALAR) {
-                const float w = __expf(s_lp[0] - s_lam[i]);
+                // the snapshot is not read again: a merge keeps the decayed key there
+                if (merge) *reinterpret_cast<float4 *>(s_ll + i * D + r0) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+            } else {
+                const float w = SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) kt[j] *= w;
+                if (merge && r0 == 0) s_w[i] = w;
             }
-            if (merge) *reinterpret_cast<float4 *>(s_lk + i * D + r0) = make_float4(kt[0], kt[1], kt[2], kt[3]);
             if constexpr (TOKEN) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -406,7 +424,8 @@ dl_step_kernel(const StepParams p) {
         if constexpr (LOG) {
             for (int i = rg; i < n; i += RG) {             // log entries as extra rows
                 const float cq = s_cq[i], ck = s_ck[i];
-                const float *u = s_lu + i * BV + cg * VEC;
+                float u[VEC];
+                lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) {
                     accq[c] += cq * u[c];
@@ -542,18 +561,13 @@ dl_step_kernel(const StepParams p) {
     if constexpr (LOG) {
         for (int i = 0; i < n; ++i) {
             float u[VEC];
-#pragma unroll
-            for (int c = 0; c < VEC; c += 4) {
-                const float4 u4 = *reinterpret_cast<const float4 *>(s_lu + i * BV + cg * VEC + c);
-                u[c] = u4.x;
-                u[c + 1] = u4.y;
-                u[c + 2] = u4.z;
-                u[c + 3] = u4.w;
-            }
+            lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
+            const float w = PERKEY ? 0.f : s_w[i];
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int r = rg + RG * j;
-                const float kt = s_lk[i * D + (r < D ? r : 0)];
+                const int rr = r < D ? r : 0;
+                const float kt = PERKEY ? s_ll[i * D + rr] : to_f32(s_lk[i * D + rr]) * w;
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) acc[j][c] += kt * u[c];
             }
