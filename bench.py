@@ -59,7 +59,8 @@ def parse(argv=None):
     ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
     ap.add_argument("--extra", default="3,4,5,g64,g128,g256,g512",
                     help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
-    ap.add_argument("--extra-steps", type=int, default=0, help="timed steps per extra workload (0 = 4 cycles)")
+    ap.add_argument("--extra-steps", type=int, default=0,
+                    help="timed steps per extra workload (0 = whole merge cycles of every rotated pool, at least 4 L)")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline runs")
     ap.add_argument("--rotate-bytes", type=float, default=1.25 * 2 ** 30,
                     help="minimum bytes of pools rotated per extra workload (cold cache)")
@@ -204,12 +205,20 @@ class Staged:
         self.bank = None
 
 
+def cycle_steps(rotate: int, L: int, at_least: int) -> int:
+    """Timed steps for `rotate` pools decoded in turn: a whole number of merge
+    cycles of every pool (rotate * L steps each), and at least `at_least`, so
+    that every measurement window holds the same mix of append and merge steps."""
+    per = rotate * L
+    return per * max(1, -(-at_least // per))
+
+
 def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native, value_tile=0, graph=True):
     """Launch mode: W warm-up steps, then K steps each bracketed by a HIP event
-    pair on the launch stream.  Graph mode: the staged steps captured once in a
+    pair on the launch stream.  Graph mode: the next K steps captured once in a
     HIP graph (the kernels read the live-log lengths on the device, so the
-    same capture is valid for every replay), replayed until about K steps ran,
-    timed by an event pair around the replays."""
+    capture stays valid for every replay), replayed once untimed and once timed
+    by an event pair around the replay."""
     st = Staged(cfg, eager, rotate, distinct, torch, dl, native, value_tile)
     try:
         st.plan_bytes(0, warmup)                 # advance the shadow schedule past warm-up
@@ -229,28 +238,22 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
                    launch_ms=[a.elapsed_time(b) for a, b in ev], dec_bytes=dec_bytes,
                    asg_bytes=asg_bytes, L=st.L, value_tile=st.value_tile, steps=steps)
         if graph:
-            S = len(st.inputs)
+            S = steps
             t0 = warmup + steps
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 st.run(t0, S)
-            reps = max(1, int(round(steps / S)))
             st.plan_bytes(t0, S)                 # the warm-up replay
             g.replay()
             torch.cuda.synchronize()
-            gb_dec, gb_asg = 0.0, 0.0
-            for _ in range(reps):
-                a, b = st.plan_bytes(t0, S)
-                gb_dec += a
-                gb_asg += b
+            gb_dec, gb_asg = st.plan_bytes(t0, S)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record()
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             e1.record()
             torch.cuda.synchronize()
-            out["graph"] = dict(ms=e0.elapsed_time(e1), steps=reps * S, dec_bytes=gb_dec, asg_bytes=gb_asg)
+            out["graph"] = dict(ms=e0.elapsed_time(e1), steps=S, dec_bytes=gb_dec, asg_bytes=gb_asg)
             del g
         return out
     finally:
@@ -431,7 +434,7 @@ def main(argv=None) -> int:
             ws = sum(dl.dl_pool_sizes(dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, c.L, c.decay,
                                                    c.update, c.state_dtype, c.in_dtype)))
             R = max(1, int(np.ceil(a.rotate_bytes / ws)))
-            xs = a.extra_steps or 4 * c.L
+            xs = a.extra_steps or cycle_steps(R, c.L, 4 * c.L)
             for eager in ([False] if a.no_eager else [False, True]):
                 rr = time_workload(c, eager, xs, c.L, R, min(4 * c.L, xs + c.L), torch, dl, native,
                                    graph=not a.no_graph)

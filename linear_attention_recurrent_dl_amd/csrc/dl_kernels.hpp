@@ -177,7 +177,10 @@ struct Tile {
     static constexpr int RPT = (D + RG - 1) / RG;          // rows per thread
     static constexpr int NW = NT / 64;                     // waves per block
     static constexpr bool RAGGED = RG > D;                 // some row groups own no row
-    static constexpr int TPE = D / 4;                      // threads per log entry (4 keys each)
+    // keys per thread in the coefficient phase (measured: 8 for fp32 state
+    // tiles, 4 for bf16 ones, whose unpacked tile leaves fewer free registers)
+    static constexpr int KPT = sizeof(ST) == 2 ? 4 : 8;
+    static constexpr int TPE = D / KPT;                    // threads per log entry
     static constexpr int EPP = NT / TPE;                   // log entries per coefficient pass
     static constexpr int PF = RPT >= 16 ? 4 : 8;           // log chunks per thread loaded up front
     static_assert(BV % VEC == 0 && D % BV == 0 && NT % CG == 0 && CG <= 64 && TPE <= 64 && NT >= D,
@@ -211,7 +214,7 @@ dl_step_kernel(const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
-    constexpr int TPE = G::TPE, EPP = G::EPP, PF = G::PF;
+    constexpr int KPT = G::KPT, TPE = G::TPE, EPP = G::EPP, PF = G::PF;
     constexpr int NV = D / BV;                    // value tiles per slot-head
     constexpr int KV = 16 / (int)sizeof(IT);      // key-factor elements per 16-byte chunk
     constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte chunk
@@ -364,39 +367,42 @@ dl_step_kernel(const StepParams p) {
     }
     __syncthreads();
 
-    // ---- 3. replay coefficients, TPE threads per entry (4 keys each):
+    // ---- 3. replay coefficients, TPE threads per entry (KPT keys each):
     //         Kt_i = e^{l' - Lam_i} * K_i (kept for a merge), c^q_i = Kt_i . q,
     //         c^k_i = Kt_i . k; the pass that reaches i == n computes a . q
     for (int i0 = 0; i0 <= n; i0 += EPP) {
         const int i = i0 + tid / TPE;
-        const int r0 = (tid % TPE) * 4;
+        const int r0 = (tid % TPE) * KPT;
         float pq = 0.f, pk = 0.f;
         if (LOG && i < n) {
-            float kt[4];
-            lds_f32<IT, 4>(s_lk + i * D + r0, kt);
-            if constexpr (PERKEY) {
-                const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + r0);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+            const float w = SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f;
+            if (!PERKEY && merge && r0 == 0) s_w[i] = w;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[r0 + j] - lv[j]);
-                // the snapshot is not read again: a merge keeps the decayed key there
-                if (merge) *reinterpret_cast<float4 *>(s_ll + i * D + r0) = make_float4(kt[0], kt[1], kt[2], kt[3]);
-            } else {
-                const float w = SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f;
+            for (int q4 = r0; q4 < r0 + KPT; q4 += 4) {
+                float kt[4];
+                lds_f32<IT, 4>(s_lk + i * D + q4, kt);
+                if constexpr (PERKEY) {
+                    const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + q4);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) kt[j] *= w;
-                if (merge && r0 == 0) s_w[i] = w;
-            }
-            if constexpr (TOKEN) {
+                    for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[q4 + j] - lv[j]);
+                    // the snapshot is not read again: a merge keeps the decayed key there
+                    if (merge) *reinterpret_cast<float4 *>(s_ll + i * D + q4) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pq += kt[j] * s_qr[r0 + j];
-                    if constexpr (DELTA) pk += kt[j] * s_a[r0 + j];
+                    for (int j = 0; j < 4; ++j) kt[j] *= w;
+                }
+                if constexpr (TOKEN) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pq += kt[j] * s_qr[q4 + j];
+                        if constexpr (DELTA) pk += kt[j] * s_a[q4 + j];
+                    }
                 }
             }
         } else if (TOKEN && i == n) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
+            for (int j = 0; j < KPT; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
         }
         if constexpr (TOKEN) {
 #pragma unroll
