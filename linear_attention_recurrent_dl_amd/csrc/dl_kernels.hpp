@@ -157,6 +157,58 @@ __device__ __forceinline__ void st16_stream(void *base, uint32_t off, const uint
     __builtin_nontemporal_store(__builtin_bit_cast(v4u32, v), reinterpret_cast<v4u32 *>(static_cast<char *>(base) + off));
 }
 
+// ---- cross-lane sums in the vector ALU (no LDS round trip): DPP moves within
+// a 16-lane row, and the gfx950 row swaps across rows.  All lanes of the wave
+// must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7 - i within each 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- 15 - i within each row
+constexpr int kDppRowRor = 0x120;         // + n: lane i <- (i + n) mod 16 within each row
+
+// x of lane i plus x of lane i ^ 16 (rows 0 <-> 1, 2 <-> 3): the swap hands
+// back both halves, whose sum is the row-pair sum in every lane.
+__device__ __forceinline__ float sum_rows_xor1(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x of lane i plus x of lane i ^ 32
+__device__ __forceinline__ float sum_rows_xor2(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64),
+// returned in every lane of the group.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (W >= 2) x += dpp_f32<kDppQuadXor1>(x);
+    if constexpr (W >= 4) x += dpp_f32<kDppQuadXor2>(x);
+    if constexpr (W >= 8) x += dpp_f32<kDppRowHalfMirror>(x);   // the other quad of the 8
+    if constexpr (W >= 16) x += dpp_f32<kDppRowMirror>(x);      // the other 8 of the row
+    if constexpr (W >= 32) x = sum_rows_xor1(x);
+    if constexpr (W >= 64) x = sum_rows_xor2(x);
+    return x;
+}
+
+// Sum over the lanes of a wave that agree modulo S (S a power of two <= 64),
+// returned in every lane: rotations by S, 2S, .. 8 close the ring of such
+// lanes inside a row, then the rows are added.
+template <int S>
+__device__ __forceinline__ float strided_sum(float x) {
+    if constexpr (S <= 1) x += dpp_f32<kDppRowRor + 1>(x);
+    if constexpr (S <= 2) x += dpp_f32<kDppRowRor + 2>(x);
+    if constexpr (S <= 4) x += dpp_f32<kDppRowRor + 4>(x);
+    if constexpr (S <= 8) x += dpp_f32<kDppRowRor + 8>(x);
+    if constexpr (S <= 16) x = sum_rows_xor1(x);
+    if constexpr (S <= 32) x = sum_rows_xor2(x);
+    return x;
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber them so that
 // each XCD works on a contiguous range of units: the value tiles and v-heads
 // of one q/k group (which share the key-log entries and q / k) then meet in
@@ -405,11 +457,8 @@ dl_step_kernel(const StepParams p) {
             for (int j = 0; j < KPT; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
         }
         if constexpr (TOKEN) {
-#pragma unroll
-            for (int off = 1; off < TPE; off <<= 1) {
-                pq += __shfl_xor(pq, off, 64);
-                if constexpr (DELTA) pk += __shfl_xor(pk, off, 64);
-            }
+            pq = group_sum<TPE>(pq);
+            if constexpr (DELTA) pk = group_sum<TPE>(pk);
             if (tid % TPE == 0) {
                 if (i < n) {
                     s_cq[i] = pq;
@@ -454,13 +503,11 @@ dl_step_kernel(const StepParams p) {
                 }
             }
         }
+        // row groups of a wave: lanes that agree modulo CG hold the same columns
 #pragma unroll
-        for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                accq[c] += __shfl_xor(accq[c], off, 64);
-                if constexpr (DELTA) acck[c] += __shfl_xor(acck[c], off, 64);
-            }
+        for (int c = 0; c < VEC; ++c) {
+            accq[c] = strided_sum<CG>(accq[c]);
+            if constexpr (DELTA) acck[c] = strided_sum<CG>(acck[c]);
         }
         if (lane < CG) {
 #pragma unroll
