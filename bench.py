@@ -2,6 +2,7 @@
 """DeltaLog decode-step benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--no-extra] [--no-cpu]
+    python bench.py --sweep merge|state
 
 A step is one decode of the workload's batch (for the serving pool: its fresh
 slot assignments, then the decode).  The headline workload is the 32-v-head
@@ -19,6 +20,13 @@ workloads and the eager baseline; there, several independent pools (layers)
 are decoded in rotation so that the working set exceeds the 256 MB Infinity
 Cache and the bytes come from HBM.  ``cpu_baseline`` times the fp64 oracle on
 the host on a bounded sample of the headline workload.
+
+``--sweep merge`` measures the merge interval M in {2, 4, 8, 16, 32, 64} at
+batch 128, d = 128, fp32 state, for each operator family (plain, GDN, GLA-style,
+KDA-style), with the eager kernel (M = 1) as reference, on cold rotated pools.
+``--sweep state`` decodes one GDN pool of 128 MiB to 1 GiB (B = 64 .. 512)
+without rotation, DeltaLog and eager, so that the Infinity Cache shows.  Each
+prints one JSON line of rows instead of the headline line.
 """
 
 from __future__ import annotations
@@ -71,6 +79,8 @@ def parse(argv=None):
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--distinct-steps", type=int, default=0,
                     help="distinct input steps staged per workload (0 = min(steps, 4 cycles))")
+    ap.add_argument("--sweep", choices=["merge", "state"], default=None,
+                    help="merge-interval or state-size sweep instead of the headline line")
     return ap.parse_args(argv)
 
 
@@ -375,6 +385,62 @@ def stream_reference(torch, mib: int = 1024, reps: int = 10):
     return {"copy_GBps": copy_gbs, "read_GBps": read_gbs, "bytes": n, "kernels": "torch copy_ / sum"}
 
 
+def pool_bytes(dl, c, L=None) -> int:
+    return sum(dl.dl_pool_sizes(dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, L or c.L, c.decay,
+                                             c.update, c.state_dtype, c.in_dtype)))
+
+
+def sweep_row(c, eager, R, torch, dl, native, graph=True):
+    L = 1 if eager else c.L
+    steps = cycle_steps(R, L, max(4 * L, 64))
+    r = time_workload(c, eager, steps, L, R, min(4 * L, steps + L, 64), torch, dl, native, graph=graph)
+    s = summarize(c, r, steps, "eager" if eager else "deltalog")
+    s["rotated_pools"] = R
+    s["pool_bytes"] = pool_bytes(dl, c, L)
+    return s
+
+
+def run_sweep(kind, a, torch, dl, native) -> dict:
+    """Merge-interval or state-size sweep (see the module docstring)."""
+    from workloads import SWEEP_OPERATORS, headline_gdn, merge_sweep_config
+    rows = []
+
+    def brief(s, **kw):
+        row = {k: s[k] for k in ("workload", "kernel", "batch", "L", "value_tile", "decode_launch_us",
+                                 "decode_GBps", "decode_frac_of_8TBps", "head_steps_per_s",
+                                 "model_bytes_per_head_step", "rotated_pools", "pool_bytes")}
+        row.update(kw)
+        print(f"[sweep] {json.dumps(row)}", file=sys.stderr, flush=True)
+        return row
+
+    if kind == "merge":
+        for op in SWEEP_OPERATORS:
+            ref = merge_sweep_config(op, 16)
+            R = max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, ref, 1))))
+            eager = brief(sweep_row(ref, True, R, torch, dl, native), op=op, M=1)
+            rows.append(eager)
+            for M in (2, 4, 8, 16, 32, 64):
+                c = merge_sweep_config(op, M)
+                try:
+                    ws = pool_bytes(dl, c)
+                except dl.DeltaLogError as err:
+                    rows.append({"op": op, "M": M, "workload": c.name, "unsupported": str(err)})
+                    print(f"[sweep] {op} M={M}: {err}", file=sys.stderr, flush=True)
+                    continue
+                R = max(1, int(np.ceil(a.rotate_bytes / ws)))
+                s = sweep_row(c, False, R, torch, dl, native)
+                rows.append(brief(s, op=op, M=M, vs_eager=eager["decode_launch_us"] / s["decode_launch_us"]))
+    else:
+        for B in (64, 128, 256, 512):
+            c = headline_gdn(B)
+            dls = brief(sweep_row(c, False, 1, torch, dl, native), base_MiB=B * c.H_v * c.d * c.d * 4 / 2 ** 20)
+            eg = brief(sweep_row(c, True, 1, torch, dl, native), base_MiB=B * c.H_v * c.d * c.d * 4 / 2 ** 20)
+            dls["vs_eager"] = eg["decode_launch_us"] / dls["decode_launch_us"]
+            rows += [dls, eg]
+    return {"sweep": kind, "unit": "us per decode step; GB/s of algorithmic bytes",
+            "peak_GBps": PEAK_HBM_GBS, "rows": rows, "kernel_source_hash": kernel_source_hash()}
+
+
 def extra_cfg(tag: str):
     from workloads import CONFIGS, headline_gdn
     if tag.startswith("g"):
@@ -401,6 +467,9 @@ def main(argv=None) -> int:
         return 1
     native.lib()
     torch.cuda.set_device(0)
+    if a.sweep:
+        print(json.dumps(run_sweep(a.sweep, a, torch, dl, native)), flush=True)
+        return 0
     cfg = extra_cfg(a.workload)
     steps, warmup = a.steps, a.warmup
     distinct = a.distinct_steps or min(steps + warmup, 4 * cfg.L)

@@ -232,3 +232,22 @@ def test_host_schedule_serving_pool_workload():
     for desc in wl2.fill_steps():
         cnt2.decode(desc.slots)
     assert np.array_equal(cnt2.n, wl2.initial_fill())
+
+
+def test_merge_sweep_shapes_validate():
+    """Every merge-sweep shape is accepted except KDA at M = 64: its 63 live
+    entries (bf16 keys, fp32 values and per-key snapshots) need 64,512 B of LDS,
+    over the 56 KiB budget, and the pool is refused up front.  GLA's bf16 value
+    factors keep the same log at 56,448 B, inside the budget."""
+    from workloads import SWEEP_OPERATORS, merge_sweep_config
+    for op in SWEEP_OPERATORS:
+        for M in (1, 2, 4, 8, 16, 32, 64):
+            c = merge_sweep_config(op, M)
+            desc = dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, M, c.decay, c.update,
+                                c.state_dtype, c.in_dtype)
+            if M == 64 and op == "kda":
+                with pytest.raises(dl.DeltaLogError) as ei:
+                    dl.dl_pool_sizes(desc)
+                assert ei.value.code == N.DL_ERR_UNSUPPORTED
+            else:
+                assert dl.dl_pool_sizes(desc)[0] == c.num_slots * c.H_v * c.d * c.d * 4

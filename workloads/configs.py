@@ -124,6 +124,26 @@ def headline_gdn(batch: int, L: int = 16, steps: int = 256, seed: int = 1100) ->
                                seed=seed + batch)
 
 
+SWEEP_OPERATORS = ("plain", "gdn", "gla", "kda")
+
+
+def merge_sweep_config(op: str, L: int, batch: int = 128) -> Config:
+    """One operator family at batch B, 32 v-heads, d = 128, fp32 state, merge
+    interval L: the shapes of the DeltaLog paper's merge-interval sweep (its
+    kernel-evaluation section sweeps M at B = 128 per operator).  Inputs keep
+    each family's workload distributions and dtypes above."""
+    if op == "gdn":
+        return dataclasses.replace(headline_gdn(batch, L=L), name=f"gdn_b{batch}_h32_d128_L{L}")
+    src = {"plain": CONFIGS[1], "gla": CONFIGS[3], "kda": CONFIGS[4]}[op]
+    kw = dict(index=200 + batch, name=f"{op}_b{batch}_h32_d128_L{L}", num_slots=batch, batch=batch,
+              H_v=32, d=128, L=L, steps=256, seed=src.seed + 7 * L)
+    if op == "plain":
+        kw.update(H_k=32, init_sigma=0.02)
+    if op == "gla":
+        kw.update(H_k=32)
+    return dataclasses.replace(src, **kw)
+
+
 def get_config(index: int) -> Config:
     return CONFIGS[index]
 
