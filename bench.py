@@ -185,8 +185,9 @@ class Staged:
             sp.decode_step(d["ids"])
         return total, assign_total
 
-    def run(self, t0: int, count: int, events=None):
-        """Launch steps t0 .. t0+count-1 on the current stream."""
+    def run(self, t0: int, count: int, events=None, decode: bool = True):
+        """Launch steps t0 .. t0+count-1 on the current stream (decode=False:
+        only their fresh-slot assignments)."""
         torch = self.torch
         stream = torch.cuda.current_stream().cuda_stream
         dec = self.lib.dl_eager_step if self.eager else self.lib.dl_decode_step
@@ -199,6 +200,8 @@ class Staged:
                          d["rep_src"], stream)
                 if rc:
                     self.N.check(rc, "dl_slot_assign")
+            if not decode:
+                continue
             if events is not None:
                 events[t - t0][0].record()
             rc = dec(pool.handle, *d["args"], stream)
@@ -265,6 +268,20 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
             torch.cuda.synchronize()
             out["graph"] = dict(ms=e0.elapsed_time(e1), steps=S, dec_bytes=gb_dec, asg_bytes=gb_asg)
             del g
+            if gb_asg > 0:
+                # the same steps' assignments alone: their replay time is taken
+                # off, leaving the decode launches' share of the step
+                ga = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(ga):
+                    st.run(t0, S, decode=False)
+                ga.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                ga.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                out["graph"]["assign_ms"] = e0.elapsed_time(e1)
+                del ga
         return out
     finally:
         st.close()
@@ -309,10 +326,14 @@ def summarize(cfg, r, steps, tag):
             bpl = gr["dec_bytes"] / gr["steps"]
             res["decode_bytes_per_launch"] = bpl
         else:
-            dec_us = launch_ms * 1e3
+            # a step is assignments + one decode launch: the decode's share is
+            # the step's replay time minus that of the assignments alone
+            dec_us = (gr["ms"] - gr["assign_ms"]) / gr["steps"] * 1e3
             res["decode_launch_us"] = dec_us
-            res["decode_launch_source"] = "event pair per launch (step also assigns fresh slots)"
-            bpl = bytes_per_launch
+            res["decode_launch_source"] = "graph replay minus an assignment-only replay of the same steps"
+            res["assign_us_per_step"] = gr["assign_ms"] / gr["steps"] * 1e3
+            bpl = gr["dec_bytes"] / gr["steps"]
+            res["decode_bytes_per_launch"] = bpl
     else:
         res.update({"ms_per_step": r["total_ms"] / steps,
                     "head_steps_per_s": res["launch_mode"]["head_steps_per_s"],
