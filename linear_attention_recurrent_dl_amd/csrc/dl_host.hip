@@ -129,11 +129,6 @@ __global__ void __launch_bounds__(256) dl_copy_state_kernel(const dl::CopyParams
 
 namespace dl {
 
-int block_threads(int D, int st) {
-    (void)st;
-    return D >= 128 ? 256 : (D >= 64 ? 128 : 64);
-}
-
 int launch_step(int D, int BV, int mode, int decay, int update, int st, int it, const StepParams &p, size_t shmem,
                 hipStream_t s) {
 #define DL_TILE(d_, bv_) \

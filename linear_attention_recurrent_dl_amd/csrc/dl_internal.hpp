@@ -94,7 +94,6 @@ inline bool value_tile_supported(int D, int BV) {
 }
 
 // Threads per block of the decode kernels for a head dim and state dtype.
-int block_threads(int D, int state_dtype);
 
 // Launch one decode / eager / merge kernel; returns hipError_t as int.
 int launch_step(int D, int BV, int mode, int decay, int update, int state_dtype, int in_dtype,
