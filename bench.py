@@ -79,8 +79,8 @@ def parse(argv=None):
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--distinct-steps", type=int, default=0,
                     help="distinct input steps staged per workload (0 = min(steps, 4 cycles))")
-    ap.add_argument("--sweep", choices=["merge", "state"], default=None,
-                    help="merge-interval or state-size sweep instead of the headline line")
+    ap.add_argument("--sweep", choices=["merge", "state", "split"], default=None,
+                    help="merge-interval, state-size or split-replay sweep instead of the headline line")
     return ap.parse_args(argv)
 
 
@@ -88,7 +88,8 @@ def parse(argv=None):
 class Staged:
     """A workload's pools and device-resident step inputs, ready to launch."""
 
-    def __init__(self, cfg, eager: bool, rotate: int, distinct: int, torch, dl, native, value_tile: int = 0):
+    def __init__(self, cfg, eager: bool, rotate: int, distinct: int, torch, dl, native, value_tile: int = 0,
+                 replay_split: bool = False):
         from workloads import Workload
         from linear_attention_recurrent_dl_amd import traffic
 
@@ -104,7 +105,7 @@ class Staged:
                                        cfg.state_dtype, cfg.in_dtype, L)
         self.pools = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
                                       cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch,
-                                      value_tile=value_tile)
+                                      value_tile=value_tile, replay_split=replay_split and not eager)
                       for _ in range(rotate)]
         self.value_tile = self.pools[0].value_tile
         self.shadow = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, L, cfg.decay, cfg.update,
@@ -226,13 +227,14 @@ def cycle_steps(rotate: int, L: int, at_least: int) -> int:
     return per * max(1, -(-at_least // per))
 
 
-def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native, value_tile=0, graph=True):
+def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native, value_tile=0, graph=True,
+                  replay_split=False):
     """Launch mode: W warm-up steps, then K steps each bracketed by a HIP event
     pair on the launch stream.  Graph mode: the next K steps captured once in a
     HIP graph (the kernels read the live-log lengths on the device, so the
     capture stays valid for every replay), replayed once untimed and once timed
     by an event pair around the replay."""
-    st = Staged(cfg, eager, rotate, distinct, torch, dl, native, value_tile)
+    st = Staged(cfg, eager, rotate, distinct, torch, dl, native, value_tile, replay_split)
     try:
         st.plan_bytes(0, warmup)                 # advance the shadow schedule past warm-up
         st.run(0, warmup)
@@ -411,11 +413,12 @@ def pool_bytes(dl, c, L=None) -> int:
                                              c.update, c.state_dtype, c.in_dtype)))
 
 
-def sweep_row(c, eager, R, torch, dl, native, graph=True):
+def sweep_row(c, eager, R, torch, dl, native, graph=True, value_tile=0, replay_split=False):
     L = 1 if eager else c.L
     steps = cycle_steps(R, L, max(4 * L, 64))
-    r = time_workload(c, eager, steps, L, R, min(4 * L, steps + L, 64), torch, dl, native, graph=graph)
-    s = summarize(c, r, steps, "eager" if eager else "deltalog")
+    r = time_workload(c, eager, steps, L, R, min(4 * L, steps + L, 64), torch, dl, native, graph=graph,
+                      value_tile=value_tile, replay_split=replay_split)
+    s = summarize(c, r, steps, "eager" if eager else ("deltalog-split" if replay_split else "deltalog"))
     s["rotated_pools"] = R
     s["pool_bytes"] = pool_bytes(dl, c, L)
     return s
@@ -451,6 +454,19 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
                 R = max(1, int(np.ceil(a.rotate_bytes / ws)))
                 s = sweep_row(c, False, R, torch, dl, native)
                 rows.append(brief(s, op=op, M=M, vs_eager=eager["decode_launch_us"] / s["decode_launch_us"]))
+    elif kind == "split":
+        # fused replay (every tile unit recomputes its slot-head's coefficients)
+        # against split ReplayPrep, by batch and tile width
+        for op, mk in (("gdn", lambda B: headline_gdn(B)), ("kda", lambda B: merge_sweep_config("kda", 16, B))):
+            for B, tiles in ((1, (32, 16)), (64, (64, 32)), (128, (64, 32))):
+                c = mk(B)
+                R = max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, c)))) if B > 1 else 1
+                for bv in tiles:
+                    fu = brief(sweep_row(c, False, R, torch, dl, native, value_tile=bv), op=op, B_V=bv)
+                    sp = brief(sweep_row(c, False, R, torch, dl, native, value_tile=bv, replay_split=True),
+                               op=op, B_V=bv)
+                    sp["split_vs_fused"] = fu["decode_launch_us"] / sp["decode_launch_us"]
+                    rows += [fu, sp]
     else:
         for B in (64, 128, 256, 512):
             c = headline_gdn(B)

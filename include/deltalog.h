@@ -88,6 +88,12 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *                   d = 32: 32; d = 16: 16.  Narrower tiles give more work
  *                   units per slot (lower latency at small batch) at the cost
  *                   of repeating the key-side replay work per tile.
+ *   replay_split    0: every value-tile work unit computes the key-side replay
+ *                   coefficients of its slot-head itself (fused).  1: a
+ *                   ReplayPrep pass computes them once per (slot, v-head) into
+ *                   the coef buffer and the append work units read them there
+ *                   ([DL] GPU-execution section, ReplayPrep -> AppendDecode);
+ *                   merging slots still replay in their own work units.
  * Factor storage follows [DL]'s operator instantiations: key factors a_t are
  * stored in in_dtype (a lossless copy of the input); value factors b_t are
  * fp32 for delta operators (cancellation-sensitive) and in_dtype for plain
@@ -105,6 +111,7 @@ typedef struct {
     int32_t state_dtype;
     int32_t in_dtype;
     int32_t value_tile;
+    int32_t replay_split;
 } dl_pool_desc;
 
 /* Device buffers of a pool, allocated by the caller with the sizes
@@ -125,6 +132,9 @@ typedef struct {
  *                                                     after entry i's own decay
  *   nlog    [P, H_v, d_v / B_V]         int32         live-log length per value tile (all
  *                                                     tiles of a slot hold the same value)
+ *   coef    [min(max_batch, launch slot limit), H_v, 2 L]  fp32   replay coefficients of
+ *                                                     one launch (replay_split only; else 0 B);
+ *                                                     transient, reused launch after launch
  * The cumulative log-decay l_bar of [DL]'s physical state is not stored: it
  * equals lamlog[n-1] when n > 0 and 0 when the log is empty. */
 typedef struct {
@@ -133,9 +143,10 @@ typedef struct {
     void    *ulog;
     float   *lamlog;
     int32_t *nlog;
+    float   *coef;
 } dl_pool_buffers;
 
-enum { DL_BUF_BASE = 0, DL_BUF_KLOG, DL_BUF_ULOG, DL_BUF_LAMLOG, DL_BUF_NLOG, DL_NUM_BUFS };
+enum { DL_BUF_BASE = 0, DL_BUF_KLOG, DL_BUF_ULOG, DL_BUF_LAMLOG, DL_BUF_NLOG, DL_BUF_COEF, DL_NUM_BUFS };
 
 typedef struct dl_pool dl_pool;
 

@@ -26,9 +26,10 @@ __all__ = ["dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign
 
 def make_desc(num_slots: int, max_batch: int, H_v: int, H_k: int, d: int, L: int,
               decay: str, update: str, state_dtype: str, in_dtype: str,
-              value_tile: int = 0) -> N.dl_pool_desc:
+              value_tile: int = 0, replay_split: int = 0) -> N.dl_pool_desc:
     return N.dl_pool_desc(num_slots, max_batch, H_v, H_k, d, d, L, DL_DECAY[decay],
-                          DL_UPDATE[update], DL_DTYPE[state_dtype], DL_DTYPE[in_dtype], value_tile)
+                          DL_UPDATE[update], DL_DTYPE[state_dtype], DL_DTYPE[in_dtype], value_tile,
+                          int(replay_split))
 
 
 def _ids(slot_ids) -> np.ndarray:
@@ -135,13 +136,15 @@ class DeltaLogPool:
 
     def __init__(self, num_slots: int, H_v: int, H_k: int, d: int, L: int, decay: str,
                  update: str, state_dtype: str = "f32", in_dtype: str = "f32",
-                 max_batch: Optional[int] = None, device="cuda", value_tile: int = 0):
+                 max_batch: Optional[int] = None, device="cuda", value_tile: int = 0,
+                 replay_split: bool = False):
         self.num_slots, self.H_v, self.H_k, self.d, self.L = num_slots, H_v, H_k, d, L
         self.decay, self.update = decay, update
         self.state_dtype, self.in_dtype = state_dtype, in_dtype
         self.max_batch = max_batch or num_slots
+        self.replay_split = bool(replay_split)
         self.desc = make_desc(num_slots, self.max_batch, H_v, H_k, d, L, decay, update,
-                              state_dtype, in_dtype, value_tile)
+                              state_dtype, in_dtype, value_tile, int(replay_split))
         self.sizes = dl_pool_sizes(self.desc)
         self.value_tile = dl_value_tile(self.desc)
         self.tiles = d // self.value_tile

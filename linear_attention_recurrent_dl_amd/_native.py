@@ -24,8 +24,8 @@ DL_ERR_DRY_RUN = -7
 DL_DECAY = {"none": 0, "scalar": 1, "per_key": 2}
 DL_UPDATE = {"plain": 0, "delta": 1}
 DL_DTYPE = {"f32": 0, "bf16": 1}
-DL_NUM_BUFS = 5
-BUF_NAMES = ("base", "klog", "ulog", "lamlog", "nlog")
+DL_NUM_BUFS = 6
+BUF_NAMES = ("base", "klog", "ulog", "lamlog", "nlog", "coef")
 
 EXPORTED = ("dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
             "dl_decode_step", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
@@ -37,12 +37,13 @@ class dl_pool_desc(ctypes.Structure):
     _fields_ = [("num_slots", c_int32), ("max_batch", c_int32), ("num_v_heads", c_int32),
                 ("num_k_heads", c_int32), ("d_k", c_int32), ("d_v", c_int32),
                 ("merge_interval", c_int32), ("decay", c_int32), ("update", c_int32),
-                ("state_dtype", c_int32), ("in_dtype", c_int32), ("value_tile", c_int32)]
+                ("state_dtype", c_int32), ("in_dtype", c_int32), ("value_tile", c_int32),
+                ("replay_split", c_int32)]
 
 
 class dl_pool_buffers(ctypes.Structure):
     _fields_ = [("base", c_void_p), ("klog", c_void_p), ("ulog", c_void_p),
-                ("lamlog", c_void_p), ("nlog", c_void_p)]
+                ("lamlog", c_void_p), ("nlog", c_void_p), ("coef", c_void_p)]
 
 
 class DeltaLogError(RuntimeError):

@@ -74,6 +74,8 @@ int validate_desc(const dl_pool_desc *d) {
     if (d->d_k != d->d_v || !supported_dim(d->d_k))
         return fail(DL_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d not built (need d_k == d_v in {16,32,64,128})",
                     d->d_k, d->d_v);
+    if (d->replay_split != 0 && d->replay_split != 1)
+        return fail(DL_ERR_INVALID_ARG, "replay_split must be 0 or 1 (got %d)", d->replay_split);
     if (d->value_tile != 0 && !dl::value_tile_supported(d->d_k, d->value_tile))
         return fail(DL_ERR_UNSUPPORTED, "value_tile %d not built for d=%d", d->value_tile, d->d_k);
     const int bv = value_tile_of(d);
@@ -97,6 +99,9 @@ void compute_sizes(const dl_pool_desc *d, size_t out[DL_NUM_BUFS]) {
     out[DL_BUF_ULOG] = P * Hv * C * D * b_size;
     out[DL_BUF_LAMLOG] = d->decay == DL_DECAY_NONE ? 0 : P * Hv * C * lam_w * 4;
     out[DL_BUF_NLOG] = P * Hv * (D / value_tile_of(d)) * 4;
+    // replay coefficients of one launch: 2 (C + 1) floats per (entry, v-head)
+    const size_t launch_slots = std::min<size_t>(d->max_batch, dl::kMaxLaunchSlots);
+    out[DL_BUF_COEF] = (d->replay_split && C > 0) ? launch_slots * Hv * 2 * (C + 1) * 4 : 0;
 }
 
 __global__ void dl_zero_i32_kernel(int32_t *p, size_t n) {
@@ -229,7 +234,8 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         if (align & 15) return fail(DL_ERR_INVALID_ARG, "token buffers must be 16-byte aligned");
 
         const int C = d.merge_interval - 1;
-        const int mode = C == 0 ? dl::MODE_EAGER : dl::MODE_STEP;
+        const bool split = d.replay_split && C > 0;
+        const int mode = C == 0 ? dl::MODE_EAGER : (split ? dl::MODE_STEP_SPLIT : dl::MODE_STEP);
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
         const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
@@ -240,9 +246,11 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         p.ulog = pool->buf.ulog;
         p.lamlog = pool->buf.lamlog;
         p.nlog = pool->buf.nlog;
+        p.coef = pool->buf.coef;
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
+        p.NV = pool->nv;
         for (int32_t lo = 0; lo < B; lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, B - lo);
             p.q = static_cast<const char *>(q) + (size_t)lo * Hk * D * s_in;
@@ -251,8 +259,15 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             p.lam = lambda ? lambda + (size_t)lo * Hv * lam_w : nullptr;
             p.beta = beta ? beta + (size_t)lo * Hv : nullptr;
             p.out = out + (size_t)lo * Hv * D;
-            p.nunits = cnt * d.num_v_heads * pool->nv;
             memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+            if (split) {
+                // ReplayPrep, one block per (entry, v-head), into the coefficient scratch
+                p.nunits = cnt * d.num_v_heads;
+                const int e = dl::launch_step(d.d_k, pool->bv, dl::MODE_REPLAY_PREP, d.decay, d.update,
+                                              d.state_dtype, d.in_dtype, p, shmem, (hipStream_t)stream);
+                if (e != hipSuccess) return hip_fail((hipError_t)e, "replay-prep kernel launch");
+            }
+            p.nunits = cnt * d.num_v_heads * pool->nv;
             const int e = dl::launch_step(d.d_k, pool->bv, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p,
                                           shmem, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail((hipError_t)e, "decode kernel launch");
@@ -286,7 +301,8 @@ int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_
     size_t sz[DL_NUM_BUFS];
     compute_sizes(desc, sz);
     if (buffers) {
-        const void *ptrs[DL_NUM_BUFS] = {buffers->base, buffers->klog, buffers->ulog, buffers->lamlog, buffers->nlog};
+        const void *ptrs[DL_NUM_BUFS] = {buffers->base, buffers->klog, buffers->ulog, buffers->lamlog, buffers->nlog,
+                                         buffers->coef};
         for (int i = 0; i < DL_NUM_BUFS; ++i) {
             if (sz[i] && !ptrs[i]) return fail(DL_ERR_INVALID_ARG, "buffer %d is NULL but needs %zu bytes", i, sz[i]);
             if ((uintptr_t)ptrs[i] & 15) return fail(DL_ERR_INVALID_ARG, "buffer %d is not 16-byte aligned", i);
@@ -382,6 +398,7 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
+        p.NV = pool->nv;
         const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
         for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
             const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);

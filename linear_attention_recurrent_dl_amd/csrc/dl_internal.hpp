@@ -19,6 +19,8 @@ enum Mode : int {
     MODE_STEP = 0,   // DeltaLog decode: append, or merge when the log is full
     MODE_EAGER = 1,  // eager read-modify-write of the dense state (no log)
     MODE_MERGE = 2,  // materialize base + log, no token
+    MODE_STEP_SPLIT = 3,  // MODE_STEP whose appending units read ReplayPrep's coefficients
+    MODE_REPLAY_PREP = 4, // ReplayPrep: key-side coefficients once per (entry, v-head)
 };
 
 enum DType : int { F32 = 0, BF16 = 1 };
@@ -38,10 +40,12 @@ struct StepParams {
     const float *lam;    // [n, H_v] | [n, H_v, D]
     const float *beta;   // [n, H_v]
     float *out;          // [n, H_v, D]
+    float *coef;         // [n, H_v, 2 (C + 1)] replay coefficients (split replay only)
     int32_t H_v;
     int32_t H_k;
     int32_t C;           // log capacity L - 1
-    int32_t nunits;      // blocks in this launch = n * H_v * (d_v / B_V)
+    int32_t NV;          // value tiles per slot-head
+    int32_t nunits;      // blocks in this launch = n * H_v * (d_v / B_V), or n * H_v (ReplayPrep)
     int32_t slots[kMaxLaunchSlots];
 };
 
@@ -92,8 +96,6 @@ inline bool value_tile_supported(int D, int BV) {
     default: return false;
     }
 }
-
-// Threads per block of the decode kernels for a head dim and state dtype.
 
 // Launch one decode / eager / merge kernel; returns hipError_t as int.
 int launch_step(int D, int BV, int mode, int decay, int update, int state_dtype, int in_dtype,

@@ -260,6 +260,71 @@ __device__ __forceinline__ void lds_f32(const T *src, float (&x)[N]) {
     }
 }
 
+// Key-side replay coefficients of a slot-head's live log ([DL] Algorithm 1,
+// ReplayPrep), TPE threads per entry with KPT keys each: the decayed key
+// Kt_i = e^{l' - Lam_i} * K_i, c^q_i = Kt_i . q and c^k_i = Kt_i . k for i < n;
+// the pass that reaches i == n computes a . q.  For a merge, Kt_i is kept in
+// the snapshot slot (per-key decay) or the entry's scalar weight in s_w.
+// Inputs in LDS: keys s_lk [n][D] as stored, snapshots s_ll [n][D] (per key)
+// or s_lam [n] (scalar), l' in s_lp, q in s_qr, a (= k) in s_a.
+template <int D, int NT, int KPT, int DECAY, bool DELTA, bool TOKEN, typename IT>
+__device__ __forceinline__ void replay_coefficients(int tid, int n, bool merge, const IT *s_lk, float *s_ll,
+                                                    const float *s_lp, const float *s_lam, const float *s_qr,
+                                                    const float *s_a, float *s_cq, float *s_ck, float *s_w,
+                                                    float &s_s) {
+    constexpr int TPE = D / KPT;                 // threads per log entry
+    constexpr int EPP = NT / TPE;                // log entries per pass
+    constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
+    constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+    for (int i0 = 0; i0 <= n; i0 += EPP) {
+        const int i = i0 + tid / TPE;
+        const int r0 = (tid % TPE) * KPT;
+        float pq = 0.f, pk = 0.f;
+        if (i < n) {
+            const float w = SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f;
+            if (!PERKEY && merge && r0 == 0) s_w[i] = w;
+#pragma unroll
+            for (int q4 = r0; q4 < r0 + KPT; q4 += 4) {
+                float kt[4];
+                lds_f32<IT, 4>(s_lk + i * D + q4, kt);
+                if constexpr (PERKEY) {
+                    const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + q4);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[q4 + j] - lv[j]);
+                    // the snapshot is not read again: a merge keeps the decayed key there
+                    if (merge) *reinterpret_cast<float4 *>(s_ll + i * D + q4) = make_float4(kt[0], kt[1], kt[2], kt[3]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) kt[j] *= w;
+                }
+                if constexpr (TOKEN) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pq += kt[j] * s_qr[q4 + j];
+                        if constexpr (DELTA) pk += kt[j] * s_a[q4 + j];
+                    }
+                }
+            }
+        } else if (TOKEN && i == n) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
+        }
+        if constexpr (TOKEN) {
+            pq = group_sum<TPE>(pq);
+            if constexpr (DELTA) pk = group_sum<TPE>(pk);
+            if (tid % TPE == 0) {
+                if (i < n) {
+                    s_cq[i] = pq;
+                    s_ck[i] = pk;
+                } else if (i == n) {
+                    s_s = pq;
+                }
+            }
+        }
+    }
+}
+
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
 dl_step_kernel(const StepParams p) {
@@ -273,6 +338,8 @@ dl_step_kernel(const StepParams p) {
     constexpr int UCH = BV / UV;                  // value-factor chunks per entry and tile
     constexpr bool TOKEN = MODE != MODE_MERGE;
     constexpr bool LOG = MODE != MODE_EAGER;
+    constexpr bool SPLIT = MODE == MODE_STEP_SPLIT;   // appends read ReplayPrep's coefficients
+    constexpr bool STEP = MODE == MODE_STEP || SPLIT;
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
     static_assert(BV % UV == 0, "value-factor chunks");
@@ -312,7 +379,8 @@ dl_step_kernel(const StepParams p) {
     if constexpr (MODE == MODE_MERGE) {
         if (n == 0) return;                             // empty log: nothing to materialize
     }
-    const bool merge = (MODE != MODE_STEP) || (n == C);
+    const bool merge = !STEP || (n == C);
+    const bool fused = !SPLIT || merge;                 // this block replays its own coefficients
 
     const IT *klog = reinterpret_cast<const IT *>(p.klog);
     const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
@@ -339,13 +407,26 @@ dl_step_kernel(const StepParams p) {
         }
     }
     if constexpr (SCALAR && LOG) {
-        if (tid < n) lam_i = lamlog[sh * C + tid];
+        if (fused && tid < n) lam_i = lamlog[sh * C + tid];
+    }
+    // split replay: this append's coefficients from the scratch (c^q, c^k per
+    // live entry, then a . q)
+    float cq_r = 0.f, ck_r = 0.f, s_r = 0.f;
+    if constexpr (SPLIT) {
+        if (!fused) {
+            const float *cf = p.coef + (size_t)eh * (2 * (C + 1));
+            if (tid < n) {
+                cq_r = cf[tid];
+                ck_r = cf[C + tid];
+            }
+            if (tid == n) s_r = cf[2 * C];
+        }
     }
     // live log as 16-byte chunks: K entries of the shared q/k head (all D keys),
     // U entries on this tile's columns, per-key snapshots (all D keys)
-    const int cK = LOG ? n * D / KV : 0;
+    const int cK = (LOG && fused) ? n * D / KV : 0;
     const int cU = LOG ? n * UCH : 0;
-    const int cL = (LOG && PERKEY) ? n * D / 4 : 0;
+    const int cL = (LOG && PERKEY && fused) ? n * D / 4 : 0;
     const int ctot = cK + cU + cL;
     // the live log lands in LDS as stored, chunk x at byte 16 x: key factors
     // [n][D], value factors on this tile [n][BV], per-key snapshots [n][D]
@@ -408,7 +489,16 @@ dl_step_kernel(const StepParams p) {
     }
     if constexpr (LOG) {
         if constexpr (SCALAR) {
-            if (tid < n) s_lam[tid] = lam_i;
+            if (fused && tid < n) s_lam[tid] = lam_i;
+        }
+        if constexpr (SPLIT) {
+            if (!fused) {
+                if (tid < n) {
+                    s_cq[tid] = cq_r;
+                    s_ck[tid] = ck_r;
+                }
+                if (tid == n) s_s = s_r;
+            }
         }
 #pragma unroll
         for (int m = 0; m < PF; ++m) {
@@ -419,55 +509,16 @@ dl_step_kernel(const StepParams p) {
     }
     __syncthreads();
 
-    // ---- 3. replay coefficients, TPE threads per entry (KPT keys each):
-    //         Kt_i = e^{l' - Lam_i} * K_i (kept for a merge), c^q_i = Kt_i . q,
-    //         c^k_i = Kt_i . k; the pass that reaches i == n computes a . q
-    for (int i0 = 0; i0 <= n; i0 += EPP) {
-        const int i = i0 + tid / TPE;
-        const int r0 = (tid % TPE) * KPT;
-        float pq = 0.f, pk = 0.f;
-        if (LOG && i < n) {
-            const float w = SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f;
-            if (!PERKEY && merge && r0 == 0) s_w[i] = w;
-#pragma unroll
-            for (int q4 = r0; q4 < r0 + KPT; q4 += 4) {
-                float kt[4];
-                lds_f32<IT, 4>(s_lk + i * D + q4, kt);
-                if constexpr (PERKEY) {
-                    const float4 l4 = *reinterpret_cast<const float4 *>(s_ll + i * D + q4);
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) kt[j] *= __expf(s_lp[q4 + j] - lv[j]);
-                    // the snapshot is not read again: a merge keeps the decayed key there
-                    if (merge) *reinterpret_cast<float4 *>(s_ll + i * D + q4) = make_float4(kt[0], kt[1], kt[2], kt[3]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) kt[j] *= w;
-                }
-                if constexpr (TOKEN) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pq += kt[j] * s_qr[q4 + j];
-                        if constexpr (DELTA) pk += kt[j] * s_a[q4 + j];
-                    }
-                }
-            }
-        } else if (TOKEN && i == n) {
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) pq += s_a[r0 + j] * s_qr[r0 + j];
-        }
-        if constexpr (TOKEN) {
-            pq = group_sum<TPE>(pq);
-            if constexpr (DELTA) pk = group_sum<TPE>(pk);
-            if (tid % TPE == 0) {
-                if (i < n) {
-                    s_cq[i] = pq;
-                    s_ck[i] = pk;
-                } else if (i == n) {
-                    s_s = pq;
-                }
-            }
-        }
+    // ---- 3. replay coefficients: computed here, or (appending units of a
+    //         split-replay launch) the ones ReplayPrep left in the scratch,
+    //         loaded with the rest of the block's inputs
+    if (fused) {
+        if constexpr (LOG)
+            replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, n, merge, s_lk, s_ll, s_lp, s_lam,
+                                                                     s_qr, s_a, s_cq, s_ck, s_w, s_s);
+        else
+            replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, 0, merge, s_lk, s_ll, s_lp, s_lam,
+                                                                     s_qr, s_a, s_cq, s_ck, s_w, s_s);
     }
     __syncthreads();
 
@@ -633,6 +684,105 @@ dl_step_kernel(const StepParams p) {
     }
 }
 
+// ReplayPrep ([DL] GPU-execution section): one block per (entry, v-head) of
+// the launch computes the key-side coefficients of the slot-head's live log
+// once and leaves them in the scratch, 2 (C + 1) floats per (entry, v-head):
+// c^q_i, then c^k_i at offset C, then a . q at offset 2 C.  Slot-heads about to
+// merge are skipped: their decode units replay in-block, since a merge needs
+// the decayed keys row by row.  Same arithmetic as the fused path.
+template <int D, int DECAY, bool DELTA, typename ST, typename IT>
+__global__ void __launch_bounds__((Tile<D, D, ST>::NT))
+dl_replay_prep_kernel(const StepParams p) {
+    using G = Tile<D, D, ST>;
+    constexpr int NT = G::NT, KPT = G::KPT;
+    constexpr int KV = 16 / (int)sizeof(IT);
+    constexpr int PF = 4;
+    constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
+    constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+
+    __shared__ float s_lp[D];
+    __shared__ float s_qr[D];
+    __shared__ float s_a[D];
+    __shared__ float s_cq[kMaxLogCap + 1];
+    __shared__ float s_ck[kMaxLogCap + 1];
+    __shared__ float s_lam[kMaxLogCap + 1];
+    __shared__ float s_w[kMaxLogCap + 1];
+    __shared__ float s_s;
+    extern __shared__ float4 s_dyn[];
+
+    const int tid = threadIdx.x;
+    const int unit = blockIdx.x;                       // (entry, v-head) of this launch
+    const int H_v = p.H_v, C = p.C;
+    const int e = unit / H_v, h = unit - e * H_v;
+    const int g = h / (H_v / p.H_k);
+    const int slot = p.slots[e];
+    const size_t sh = (size_t)slot * H_v + h;
+    const size_t gk = (size_t)slot * p.H_k + g;
+    const int n = p.nlog[sh * p.NV];                   // every tile of the slot-head holds the same
+    if (n == C) return;
+
+    float qv = 0.f, kv = 0.f, lam = 0.f, lbar = 0.f, lam_i = 0.f;
+    if (tid < D) {
+        const size_t qo = ((size_t)e * p.H_k + g) * D + tid;
+        qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+        kv = to_f32(reinterpret_cast<const IT *>(p.k)[qo]);
+        if constexpr (SCALAR) lam = p.lam[(size_t)e * H_v + h];
+        if constexpr (PERKEY) lam = p.lam[((size_t)e * H_v + h) * D + tid];
+        if (n > 0) {
+            if constexpr (SCALAR) lbar = p.lamlog[sh * C + (n - 1)];
+            if constexpr (PERKEY) lbar = p.lamlog[(sh * C + (n - 1)) * D + tid];
+        }
+    }
+    if constexpr (SCALAR) {
+        if (tid < n) lam_i = p.lamlog[sh * C + tid];
+    }
+    // key entries of the q/k head, then per-key snapshots, as stored, chunk x at byte 16 x
+    const int cK = n * D / KV;
+    const int ctot = cK + (PERKEY ? n * D / 4 : 0);
+    char *s_log = reinterpret_cast<char *>(s_dyn);
+    const IT *s_lk = reinterpret_cast<const IT *>(s_log);
+    float *s_ll = reinterpret_cast<float *>(s_log + (size_t)cK * 16);
+    const uint4 *kb = reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.klog) + gk * C * D);
+    const uint4 *lb = reinterpret_cast<const uint4 *>(p.lamlog + sh * C * D);
+    auto chunk_ptr = [&](int x) -> const uint4 * { return x < cK ? kb + x : lb + (x - cK); };
+    uint4 pf[PF];
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+        const int x = tid + m * NT;
+        if (x < ctot) pf[m] = *chunk_ptr(x);
+    }
+    if (tid < D) {
+        s_lp[tid] = lbar + lam;
+        s_qr[tid] = qv;
+        s_a[tid] = kv;
+    }
+    if constexpr (SCALAR) {
+        if (tid < n) s_lam[tid] = lam_i;
+    }
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+        const int x = tid + m * NT;
+        if (x < ctot) {
+            const uint4 w = pf[m];
+            *reinterpret_cast<uint4 *>(s_log + (size_t)x * 16) = make_uint4(w.x, w.y, w.z, w.w);
+        }
+    }
+    for (int x = tid + PF * NT; x < ctot; x += NT) {
+        const uint4 w = *chunk_ptr(x);
+        *reinterpret_cast<uint4 *>(s_log + (size_t)x * 16) = make_uint4(w.x, w.y, w.z, w.w);
+    }
+    __syncthreads();
+    replay_coefficients<D, NT, KPT, DECAY, DELTA, true, IT>(tid, n, false, s_lk, s_ll, s_lp, s_lam, s_qr, s_a,
+                                                             s_cq, s_ck, s_w, s_s);
+    __syncthreads();
+    float *cf = p.coef + (size_t)unit * (2 * (C + 1));
+    for (int i = tid; i < n; i += NT) {
+        cf[i] = s_cq[i];
+        cf[C + i] = s_ck[i];
+    }
+    if (tid == 0) cf[2 * C] = s_s;
+}
+
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT>
 static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipStream_t s) {
     constexpr int NT = Tile<D, BV, ST>::NT;
@@ -646,6 +796,12 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
         break;
     case MODE_MERGE:
         dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p);
+        break;
+    case MODE_STEP_SPLIT:
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p);
+        break;
+    case MODE_REPLAY_PREP:
+        dl_replay_prep_kernel<D, DECAY, DELTA, ST, IT><<<grid, block, shmem, s>>>(p);
         break;
     default:
         return hipErrorInvalidValue;

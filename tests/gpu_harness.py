@@ -62,7 +62,7 @@ class Result:
 
 def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int] = None,
         eager: bool = False, merge_every: int = 0, check_klog: bool = True,
-        value_tile: int = 0) -> Result:
+        value_tile: int = 0, replay_split: bool = False) -> Result:
     """Decode ``cfg`` on the GPU and in the oracle; compare outputs of tracked
     entries every step, the final state of tracked slots after a flush, the
     schedule of every entry, and the device counters of every slot."""
@@ -70,9 +70,11 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
     P, Hv, Hk, D = cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d
     track = list(range(P)) if track is None else sorted(int(s) for s in track)
     L = 1 if eager else cfg.L
-    say(f"[gpu] {cfg.describe()} eager={eager} track={len(track)} slots value_tile={value_tile}")
+    say(f"[gpu] {cfg.describe()} eager={eager} track={len(track)} slots value_tile={value_tile} "
+        f"replay_split={replay_split}")
     pool = dl.DeltaLogPool(P, Hv, Hk, D, L, cfg.decay, cfg.update, cfg.state_dtype,
-                           cfg.in_dtype, max_batch=cfg.batch, value_tile=value_tile)
+                           cfg.in_dtype, max_batch=cfg.batch, value_tile=value_tile,
+                           replay_split=replay_split)
     st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
     # initial states: every slot gets its seeded base (chunks of max_batch)
     for lo in range(0, P, cfg.batch):

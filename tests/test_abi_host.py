@@ -60,7 +60,12 @@ def test_pool_sizes_formula():
         wide = 64 if (D == 128 and cfg.state_dtype == "f32") else D
         assert bv == (32 if (D >= 64 and cfg.batch * Hv * (D // wide) < 256) else wide), cfg.name
         assert sz == [P * Hv * D * D * s_st, P * Hk * C * D * s_in, P * Hv * C * D * s_b,
-                      P * Hv * C * lam_w * 4, P * Hv * (D // bv) * 4], cfg.name
+                      P * Hv * C * lam_w * 4, P * Hv * (D // bv) * 4, 0], cfg.name
+        # split replay adds one launch's coefficient scratch: 2 L floats per (entry, v-head)
+        split = dl.make_desc(cfg.num_slots, cfg.batch, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay,
+                             cfg.update, cfg.state_dtype, cfg.in_dtype, replay_split=1)
+        launch_slots = min(cfg.batch, dl.dl_launch_slot_limit())
+        assert dl.dl_pool_sizes(split) == sz[:5] + [launch_slots * Hv * 2 * cfg.L * 4], cfg.name
 
 
 @pytest.mark.parametrize("d,bv,ok", [(128, 128, True), (128, 64, True), (128, 32, True), (128, 16, True),
@@ -87,6 +92,7 @@ def test_value_tile_choices(d, bv, ok):
     ("decay", 7, N.DL_ERR_INVALID_ARG),
     ("update", 2, N.DL_ERR_INVALID_ARG),
     ("state_dtype", 5, N.DL_ERR_INVALID_ARG),
+    ("replay_split", 2, N.DL_ERR_INVALID_ARG),
     ("d_k", 48, N.DL_ERR_UNSUPPORTED),
     ("d_v", 32, N.DL_ERR_UNSUPPORTED),                # d_k != d_v
 ])

@@ -15,8 +15,9 @@ from workloads import CONFIGS, Workload, small_variant
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("idx,value_tile", [(2, 0), (2, 32), (4, 0), (5, 0)])
-def test_graph_replay_matches_oracle(idx, value_tile):
+@pytest.mark.parametrize("idx,value_tile,split", [(2, 0, False), (2, 32, False), (4, 0, False), (5, 0, False),
+                                                 (2, 32, True), (4, 32, True)])
+def test_graph_replay_matches_oracle(idx, value_tile, split):
     import torch
 
     import linear_attention_recurrent_dl_amd as dl
@@ -29,12 +30,12 @@ def test_graph_replay_matches_oracle(idx, value_tile):
     if base.random_slots:
         kw["num_slots"] = 3
     cfg = small_variant(base, **kw)
-    say(f"[gpu] graph replay {cfg.describe()} value_tile={value_tile}")
+    say(f"[gpu] graph replay {cfg.describe()} value_tile={value_tile} replay_split={split}")
     wl = Workload(cfg)
     st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
     P = cfg.num_slots
     pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
-                           cfg.in_dtype, max_batch=cfg.batch, value_tile=value_tile)
+                           cfg.in_dtype, max_batch=cfg.batch, value_tile=value_tile, replay_split=split)
     ids = np.arange(P, dtype=np.int32)
     pool.assign(ids, to_dev(wl.init_base(ids), st))
     E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))

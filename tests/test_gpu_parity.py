@@ -148,3 +148,41 @@ def test_value_tiles_headline_gdn(bv):
     from gpu_harness import run
     cfg = CONFIGS[2]
     _check(cfg, run(cfg, value_tile=bv))
+
+
+# ---- split replay: ReplayPrep computes the key-side coefficients once per
+#      (slot, v-head) into the scratch, the appending tile units read them
+#      ([DL] GPU-execution section); merging slots still replay in-block
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: "-".join(c))
+def test_split_replay_operator_dtype_matrix(combo):
+    from gpu_harness import run
+    decay, update, st, it = combo
+    cfg = small_variant(CONFIGS[4], batch=3, steps=23, L=5, d=64, H_v=4, H_k=2, decay=decay,
+                        update=update, state_dtype=st, in_dtype=it,
+                        name=f"split_matrix_{decay}_{update}_{st}_{it}",
+                        qk_dist="unit" if update == "delta" else "normal_scaled",
+                        qk_scale=0.25, v_scale=1.0 if update == "delta" else 0.25,
+                        lam_mu=None if decay == "none" else 3.0,
+                        lam_sigma=None if decay == "none" else 1.0,
+                        beta=update == "delta", init_sigma=0.02)
+    _check(cfg, run(cfg, value_tile=32, replay_split=True))
+
+
+@pytest.mark.parametrize("d,bv", [(128, 64), (128, 32), (128, 16), (64, 32)])
+@pytest.mark.parametrize("base_idx", [2, 3, 4, 5])
+def test_split_replay_value_tiles(d, bv, base_idx):
+    from gpu_harness import run
+    base = CONFIGS[base_idx]
+    kw = dict(batch=3, steps=2 * base.L + 5, d=d, H_v=4, H_k=2 if base.H_k < base.H_v else 4,
+              name=f"split_{base.name}_d{d}_bv{bv}")
+    if base.random_slots:
+        kw.update(num_slots=9, replace_per_step=1)
+    cfg = small_variant(base, **kw)
+    _check(cfg, run(cfg, value_tile=bv, merge_every=7, replay_split=True))
+
+
+def test_split_replay_headline_gdn():
+    """The batch-1 GDN workload, 32-column tiles (four per head), every output compared."""
+    from gpu_harness import run
+    cfg = CONFIGS[2]
+    _check(cfg, run(cfg, value_tile=32, replay_split=True))
