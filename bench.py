@@ -24,8 +24,10 @@ the host on a bounded sample of the headline workload.
 ``--sweep merge`` measures the merge interval M in {2, 4, 8, 16, 32, 64} at
 batch 128, d = 128, fp32 state, for each operator family (plain, GDN, GLA-style,
 KDA-style), with the eager kernel (M = 1) as reference, on cold rotated pools.
-``--sweep state`` decodes one GDN pool of 128 MiB to 1 GiB (B = 64 .. 512)
-without rotation, DeltaLog and eager, so that the Infinity Cache shows.  Each
+``--sweep state`` decodes one pool of 128 MiB to 1 GiB (B = 64 .. 512, d = 128,
+fp32) per family (GDN, KDA-style, GLA-style) without rotation, DeltaLog and
+eager, so that the Infinity Cache shows.  ``--sweep split`` compares fused
+replay with split ReplayPrep by batch and value-tile width.  Each
 prints one JSON line of rows instead of the headline line.
 """
 
@@ -468,12 +470,14 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
                     sp["split_vs_fused"] = fu["decode_launch_us"] / sp["decode_launch_us"]
                     rows += [fu, sp]
     else:
-        for B in (64, 128, 256, 512):
-            c = headline_gdn(B)
-            dls = brief(sweep_row(c, False, 1, torch, dl, native), base_MiB=B * c.H_v * c.d * c.d * 4 / 2 ** 20)
-            eg = brief(sweep_row(c, True, 1, torch, dl, native), base_MiB=B * c.H_v * c.d * c.d * 4 / 2 ** 20)
-            dls["vs_eager"] = eg["decode_launch_us"] / dls["decode_launch_us"]
-            rows += [dls, eg]
+        for op in ("gdn", "kda", "gla"):
+            for B in (64, 128, 256, 512):
+                c = headline_gdn(B) if op == "gdn" else merge_sweep_config(op, 16, B)
+                mib = B * c.H_v * c.d * c.d * 4 / 2 ** 20
+                dls = brief(sweep_row(c, False, 1, torch, dl, native), op=op, base_MiB=mib)
+                eg = brief(sweep_row(c, True, 1, torch, dl, native), op=op, base_MiB=mib)
+                dls["vs_eager"] = eg["decode_launch_us"] / dls["decode_launch_us"]
+                rows += [dls, eg]
     return {"sweep": kind, "unit": "us per decode step; GB/s of algorithmic bytes",
             "peak_GBps": PEAK_HBM_GBS, "rows": rows, "kernel_source_hash": kernel_source_hash()}
 

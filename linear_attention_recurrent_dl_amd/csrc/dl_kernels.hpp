@@ -7,34 +7,37 @@
 // Accelerator for Memory-Bound Linear Attention Decode on FPGA" -- grouped
 // value heads.
 //
-// One block owns the d_k x B_V value tile of one (slot, v-head) pair.  Every
-// block of a slot-head computes the (cheap) key-side replay coefficients
-// itself -- the paper's ReplayPrep -- and owns its own live-length counter,
+// One block owns the d_k x B_V value tile of one (slot, v-head) pair.  Each
+// block computes the key-side replay coefficients of its slot-head itself (the
+// paper's ReplayPrep, fused) and owns its own live-length counter (Finalize),
 // so nothing is shared between blocks within a launch except the key entry
-// and decay snapshot, which only the first tile writes (the paper's
-// designated writer; Finalize becomes each block's own counter write).  No
-// scratch buffer and no second launch.  Per block:
+// and decay snapshot, which only the first tile writes (the designated
+// writer).  Per block:
 //
-//   1. issue the base-tile loads: every thread holds RPT rows x VEC columns as
-//      16-byte vectors; for a fixed row index the block reads NT x 16
-//      contiguous bytes (fully coalesced, one pass over the base)
+//   1. issue every load before consuming any: token inputs, the live log as
+//      16-byte chunks, then the base tile (RPT x 16-byte non-temporal loads
+//      per thread over one contiguous run; the base is value-tile major)
 //   2. l' = l_bar + lambda (l_bar = newest snapshot, or 0 for an empty log);
-//      q~ = e^{l'} * q and k~ = e^{l'} * k go to LDS
-//   3. replay coefficients per live entry i (one wave per entry, cross-lane
-//      sums): c^q_i = sum_r e^{l'_r - Lam_ir} K_ir q_r, c^k_i likewise with k,
-//      and the merge-time key factors e^{l' - Lam_i} * K_i into LDS
+//      q~ = e^{l'} * q and k~ = e^{l'} * k go to LDS, the log lands in LDS as
+//      stored
+//   3. replay coefficients per live entry i (TPE threads per entry, DPP sums):
+//      c^q_i = sum_r e^{l'_r - Lam_ir} K_ir q_r, c^k_i likewise with k, and
+//      for a merge the decayed keys e^{l' - Lam_i} * K_i
 //   4. y_q = S_bar^T q~ + sum_i c^q_i U_i and y_k = S_bar^T k~ + sum_i c^k_i U_i:
-//      per-thread FMAs over its rows, then xor-shuffles across the row groups
-//      of a wave and an LDS sum across waves
+//      per-thread FMAs over its rows, DPP / row-swap sums across the row
+//      groups of a wave, an LDS sum across waves
 //   5. per column: b = beta (v - y_k) (delta) or the given b; o = y_q + (a.q) b
-//   6. append: write U[n] <- b, K[n] <- a (the first v-head of a q/k group
-//      owns the shared key entry), Lam[n] <- l', n <- n + 1
+//   6. append: U[n] <- b, K[n] <- a (the first v-head of a q/k group owns the
+//      shared key entry), Lam[n] <- l', n <- n + 1
 //      merge:  S_bar <- e^{l'} * S_bar + sum_i (e^{l'-Lam_i} K_i) U_i^T + a b^T
 //      from the tile still in registers, n <- 0
 //
 // The eager baseline is the same block with no log: always step 6's merge
 // branch with n = 0, i.e. read S, decay, correct, add the outer product, write
 // S.  The standalone merge uses the same code with no token (lambda = 0).
+// Split replay (a pool option) moves step 3 of appending slot-heads into a
+// ReplayPrep kernel that runs once per (slot, v-head) and leaves the
+// coefficients in a scratch buffer.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,51 +61,6 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     uint32_t u = __float_as_uint(x);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (bf16_t)(u >> 16);
-}
-
-// N consecutive elements of T starting at p (N * sizeof(T) in {4, 8, 16, 32}
-// bytes, p aligned to that size up to 16), widened to fp32.
-template <typename T, int N>
-__device__ __forceinline__ void load_f32(const T *__restrict__ p, float (&out)[N]) {
-    constexpr int BYTES = N * (int)sizeof(T);
-    static_assert(BYTES % 4 == 0, "vector of at least 4 bytes");
-    if constexpr (BYTES >= 16) {
-        const uint4 *v = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-        for (int c = 0; c < BYTES / 16; ++c) {
-            uint4 w = v[c];
-            uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (sizeof(T) == 4) {
-                    out[c * 4 + j] = __uint_as_float(ws[j]);
-                } else {
-                    out[c * 8 + 2 * j] = __uint_as_float(ws[j] << 16);
-                    out[c * 8 + 2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
-                }
-            }
-        }
-    } else if constexpr (BYTES == 8) {
-        uint2 w = *reinterpret_cast<const uint2 *>(p);
-        uint32_t ws[2] = {w.x, w.y};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if constexpr (sizeof(T) == 4) {
-                out[j] = __uint_as_float(ws[j]);
-            } else {
-                out[2 * j] = __uint_as_float(ws[j] << 16);
-                out[2 * j + 1] = __uint_as_float(ws[j] & 0xFFFF0000u);
-            }
-        }
-    } else {
-        uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-        if constexpr (sizeof(T) == 4) {
-            out[0] = __uint_as_float(w);
-        } else {
-            out[0] = __uint_as_float(w << 16);
-            out[1] = __uint_as_float(w & 0xFFFF0000u);
-        }
-    }
 }
 
 // Unpack a 16-byte register vector of T into fp32.
