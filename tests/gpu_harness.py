@@ -57,6 +57,9 @@ class Result:
     merges: int = 0
     appends: int = 0
     steps: int = 0
+    compared_outputs: int = 0      # output values compared with the oracle
+    expected_outputs: int = 0      # decoded entries of tracked slots x H_v x d
+    compared_states: int = 0       # final-state values compared
     extra: Dict[str, float] = field(default_factory=dict)
 
 
@@ -111,6 +114,7 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
         beta = to_dev(inp.beta, torch.float32)
         out = step_fn(ids, q, k, v, lam, beta)
         sel, o_ref = E.step(ids, inp.q, inp.k, inp.v, inp.lam, inp.beta)
+        res.expected_outputs += sum(int(s) in tracked for s in ids) * Hv * D
         if len(sel):
             o_gpu = out[torch.from_numpy(sel).to(DEV)].cpu().numpy()
             out_e.add(o_gpu, o_ref)
@@ -146,6 +150,7 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
     st_e = RelL2()
     st_e.add(S_gpu, E.states())
     res.out_err, res.state_err = out_e.value, st_e.value
+    res.compared_outputs, res.compared_states = out_e.count, st_e.count
     say(f"[gpu]   out rel-L2 {res.out_err:.3e}  state rel-L2 {res.state_err:.3e}  "
         f"merges {res.merges} appends {res.appends}  sched-mismatch {res.sched_mismatch}  "
         f"counter-mismatch {res.counter_mismatch}  klog-mismatch {res.klog_mismatch}")

@@ -16,6 +16,9 @@ pytestmark = pytest.mark.gpu
 def _check(cfg, res):
     from gpu_harness import tolerance
     tol = tolerance(cfg)
+    # every decoded entry of a tracked slot was compared, and some state
+    assert res.compared_outputs == res.expected_outputs > 0
+    assert res.compared_states > 0
     assert res.sched_mismatch == 0
     assert res.counter_mismatch == 0
     assert res.klog_mismatch == 0

@@ -98,3 +98,62 @@ def test_fpga_table2_state_bytes():
     tok = traffic.token_bytes(H_v=g["h_v"], H_k=16, d_k=g["d"], d_v=g["d"], in_bytes=4,
                               per_head_scalars=4)
     assert tok == g["token_io_bytes"]
+
+
+# ---- the comparison machinery itself: a wrong metric or a wrong entry
+#      selection would let every parity test pass without comparing anything
+def test_rel_l2_metric_values():
+    from oracle import RelL2
+    rng = np.random.default_rng(11)
+    ref = rng.standard_normal((3, 4, 5))
+    m = RelL2()
+    m.add(ref, ref)
+    assert m.value == 0.0 and m.count == ref.size
+    m = RelL2()
+    m.add(2.0 * ref, ref)                       # ||2r - r|| / ||r|| = 1
+    assert abs(m.value - 1.0) < 1e-15
+    # streaming over pieces equals one pass over the concatenation
+    x = ref + 1e-3 * rng.standard_normal(ref.shape)
+    whole = RelL2()
+    whole.add(x, ref)
+    parts = RelL2()
+    parts.add(x[:1], ref[:1])
+    parts.add(x[1:], ref[1:])
+    direct = np.linalg.norm((x - ref).ravel()) / np.linalg.norm(ref.ravel())
+    assert abs(whole.value - direct) < 1e-15 and abs(parts.value - direct) < 1e-15
+    # a NaN or an all-zero reference with a nonzero result never passes a bound
+    bad = RelL2()
+    bad.add(np.full(3, np.nan), np.ones(3))
+    assert not (bad.value <= 1e-4)
+    z = RelL2()
+    z.add(np.ones(2), np.zeros(2))
+    assert not (z.value <= 1e-4)
+    with pytest.raises(ValueError):
+        RelL2().add(np.ones(3), np.ones(4))
+
+
+def test_eager_pool_steps_exactly_the_tracked_entries():
+    """EagerPool follows a subset of slots: its outputs and states equal the
+    eager recurrence run on exactly those batch entries, in batch order."""
+    from oracle import EagerPool
+    from oracle.recurrence import eager_step
+    rng = np.random.default_rng(12)
+    H_v, d = 2, 4
+    P = 6
+    init = rng.standard_normal((P, H_v, d, d))
+    tracked = [4, 1, 3]
+    E = EagerPool(tracked, H_v, d, d, "scalar", "delta", init=init[tracked])
+    S_all = init.copy()
+    for t in range(4):
+        ids = rng.permutation(P)[:4]
+        q, k, v = (rng.standard_normal((4, H_v, d)) for _ in range(3))
+        lam = -rng.random((4, H_v))
+        beta = rng.random((4, H_v))
+        sel, o = E.step(ids, q, k, v, lam, beta)
+        want = [j for j, s in enumerate(ids) if s in tracked]
+        assert sel.tolist() == want and o.shape == (len(want), H_v, d)
+        S_new, o_all = eager_step(S_all[ids], q, k, v, lam, beta, "scalar", "delta")
+        S_all[ids] = S_new
+        assert np.allclose(o, o_all[want], rtol=0, atol=1e-13)
+    assert np.allclose(E.states(), S_all[tracked], rtol=0, atol=1e-13)
+    assert np.allclose(E.states([3]), S_all[[3]], rtol=0, atol=1e-13)
