@@ -189,3 +189,22 @@ def test_split_replay_headline_gdn():
     from gpu_harness import run
     cfg = CONFIGS[2]
     _check(cfg, run(cfg, value_tile=32, replay_split=True))
+
+
+# ---- edge shapes: the longest log (63 live entries, past the up-front
+#      prefetch, so the remainder staging loop runs) at d = 128, and eight
+#      v-heads sharing one q/k head (one designated key writer per group)
+@pytest.mark.parametrize("base_idx,bv", [(2, 64), (2, 32), (4, 64)])
+def test_longest_log_d128(base_idx, bv):
+    from gpu_harness import run
+    base = CONFIGS[base_idx]
+    cfg = small_variant(base, batch=2, steps=140, L=64 if base.decay != "per_key" else 32, d=128, H_v=4,
+                        H_k=2 if base.H_k < base.H_v else 4, name=f"longlog_{base.name}_bv{bv}")
+    _check(cfg, run(cfg, value_tile=bv))
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_eight_v_heads_per_qk_head(split):
+    from gpu_harness import run
+    cfg = small_variant(CONFIGS[2], batch=3, steps=37, L=6, d=64, H_v=16, H_k=2, name="gva8")
+    _check(cfg, run(cfg, value_tile=32, replay_split=split))
