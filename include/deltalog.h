@@ -69,7 +69,8 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
 /* Pool descriptor, fixed at creation ([DL] serving-integration section: each
  * slot carries a dense base plus bounded key/value logs, log-decay snapshots
  * and live-log metadata).
- *   num_slots       P, slots in the pool (requests x layers a caller maps here)
+ *   num_slots       P, slots in the pool (requests x layers a caller maps here),
+ *                   1 <= P <= 2^24
  *   max_batch       largest B of one dl_decode_step / dl_slot_assign / dl_merge
  *   num_v_heads     H_v;  num_k_heads H_k (H_v % H_k == 0; grouped value heads)
  *   d_k, d_v        head dims; this build supports d_k == d_v in {16, 32, 64, 128}

@@ -57,7 +57,8 @@ int value_tile_of(const dl_pool_desc *d) {
 
 int validate_desc(const dl_pool_desc *d) {
     if (!d) return fail(DL_ERR_INVALID_ARG, "desc is NULL");
-    if (d->num_slots < 1) return fail(DL_ERR_INVALID_ARG, "num_slots must be >= 1 (got %d)", d->num_slots);
+    if (d->num_slots < 1 || d->num_slots > dl::kMaxSlots)
+        return fail(DL_ERR_INVALID_ARG, "num_slots must be in [1, %d] (got %d)", dl::kMaxSlots, d->num_slots);
     if (d->max_batch < 1) return fail(DL_ERR_INVALID_ARG, "max_batch must be >= 1 (got %d)", d->max_batch);
     if (d->num_v_heads < 1 || d->num_k_heads < 1)
         return fail(DL_ERR_INVALID_ARG, "head counts must be >= 1 (H_v=%d, H_k=%d)", d->num_v_heads, d->num_k_heads);
@@ -260,6 +261,10 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             p.beta = beta ? beta + (size_t)lo * Hv : nullptr;
             p.out = out + (size_t)lo * Hv * D;
             memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+            if (mode == dl::MODE_STEP) {         // the host's live lengths ride in the slot words
+                for (int32_t j = 0; j < cnt; ++j)
+                    p.slots[j] |= (uint32_t)pool->n[ids[lo + j]] << dl::kSlotBits;
+            }
             if (split) {
                 // ReplayPrep, one block per (entry, v-head), into the coefficient scratch
                 p.nunits = cnt * d.num_v_heads;

@@ -15,6 +15,13 @@ constexpr int kMaxLaunchSlots = 512;
 // Largest log capacity C = L - 1 (sizes the per-block coefficient arrays).
 constexpr int kMaxLogCap = 63;
 
+// A launch's slot word: the slot id in the low 24 bits; a decode launch puts
+// the host's live length of the slot (<= kMaxLogCap) in the top 8, so that one
+// scalar argument load brings both.
+constexpr int kSlotBits = 24;
+constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1;
+constexpr int kMaxSlots = 1 << kSlotBits;
+
 enum Mode : int {
     MODE_STEP = 0,   // DeltaLog decode: append, or merge when the log is full
     MODE_EAGER = 1,  // eager read-modify-write of the dense state (no log)
@@ -46,7 +53,7 @@ struct StepParams {
     int32_t C;           // log capacity L - 1
     int32_t NV;          // value tiles per slot-head
     int32_t nunits;      // blocks in this launch = n * H_v * (d_v / B_V), or n * H_v (ReplayPrep)
-    int32_t slots[kMaxLaunchSlots];
+    uint32_t slots[kMaxLaunchSlots];   // slot words (see kSlotBits)
 };
 
 // Arguments of the state-copy kernel (slot assignment and base read-back):

@@ -298,6 +298,7 @@ dl_step_kernel(const StepParams p) {
     constexpr bool LOG = MODE != MODE_EAGER;
     constexpr bool SPLIT = MODE == MODE_STEP_SPLIT;   // appends read ReplayPrep's coefficients
     constexpr bool STEP = MODE == MODE_STEP || SPLIT;
+    constexpr bool HINTED = MODE == MODE_STEP;        // loads follow the host's live length
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
     static_assert(BV % UV == 0, "value-factor chunks");
@@ -326,18 +327,32 @@ dl_step_kernel(const StepParams p) {
     const int e = eh / H_v, h = eh - e * H_v;
     const int c0 = vt * BV;                             // first column of the tile
     const int grp = H_v / p.H_k, g = h / grp;
-    const int slot = p.slots[e];
+    const uint32_t sword = p.slots[e];
+    const int slot = (int)(sword & kSlotMask);
     const size_t sh = (size_t)slot * H_v + h;           // slot-head index
     const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
     const int cg = tid % CG, rg = tid / CG;
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
-    int n = 0;
-    if constexpr (LOG) n = p.nlog[sh * NV + vt];
+    // Live length n.  A decode launch takes the host's value for the slot (the
+    // slot word's top byte), so that no load below waits for the device
+    // counter; the counter, read alongside, decides (step 2 stages again when
+    // the two differ, as when a captured step is replayed from another phase).
+    // Its index is made opaque to keep it a vector load: a scalar one would
+    // order the scalar argument loads behind it.
+    int n = 0, n_dev = 0;
+    if constexpr (HINTED) {
+        n = min((int)(sword >> kSlotBits), C);
+        int ni = (int)(sh * NV + vt);
+        asm volatile("" : "+v"(ni));
+        n_dev = p.nlog[ni];
+    } else if constexpr (LOG) {
+        n = p.nlog[sh * NV + vt];
+    }
     if constexpr (MODE == MODE_MERGE) {
         if (n == 0) return;                             // empty log: nothing to materialize
     }
-    const bool merge = !STEP || (n == C);
+    bool merge = !STEP || (n == C);
     const bool fused = !SPLIT || merge;                 // this block replays its own coefficients
 
     const IT *klog = reinterpret_cast<const IT *>(p.klog);
@@ -382,17 +397,23 @@ dl_step_kernel(const StepParams p) {
     }
     // live log as 16-byte chunks: K entries of the shared q/k head (all D keys),
     // U entries on this tile's columns, per-key snapshots (all D keys)
-    const int cK = (LOG && fused) ? n * D / KV : 0;
-    const int cU = LOG ? n * UCH : 0;
-    const int cL = (LOG && PERKEY && fused) ? n * D / 4 : 0;
-    const int ctot = cK + cU + cL;
     // the live log lands in LDS as stored, chunk x at byte 16 x: key factors
     // [n][D], value factors on this tile [n][BV], per-key snapshots [n][D]
     // (overwritten by e^{l'-Lam_i} * K_i for a merge)
     char *s_log = reinterpret_cast<char *>(s_dyn);
     const IT *s_lk = reinterpret_cast<const IT *>(s_log);
-    const BT *s_lu = reinterpret_cast<const BT *>(s_log + (size_t)cK * 16);
-    float *s_ll = reinterpret_cast<float *>(s_log + (size_t)(cK + cU) * 16);
+    int cK = 0, cU = 0, ctot = 0;
+    const BT *s_lu = nullptr;
+    float *s_ll = nullptr;
+    auto log_layout = [&]() {
+        cK = (LOG && fused) ? n * D / KV : 0;
+        cU = LOG ? n * UCH : 0;
+        const int cL = (LOG && PERKEY && fused) ? n * D / 4 : 0;
+        ctot = cK + cU + cL;
+        s_lu = reinterpret_cast<const BT *>(s_log + (size_t)cK * 16);
+        s_ll = reinterpret_cast<float *>(s_log + (size_t)(cK + cU) * 16);
+    };
+    log_layout();
     const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gk * C * D);
     const BT *ub = ulog + sh * C * D + c0;
     const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + sh * C * D);
@@ -432,8 +453,8 @@ dl_step_kernel(const StepParams p) {
     }
 
     // ---- 2. decay bookkeeping, decayed q / k, and the log into LDS
-    if (tid < D) {
-        const float lp = lbar + lam;                    // l' = l_bar + lambda
+    auto stage_decay = [&](const float lb) {            // rows tid < D
+        const float lp = lb + lam;                      // l' = l_bar + lambda
         const float gg = (DECAY == DECAY_NONE) ? 1.f : __expf(lp);
         s_lp[tid] = lp;
         s_g[tid] = gg;
@@ -444,7 +465,8 @@ dl_step_kernel(const StepParams p) {
             s_k[tid] = gg * kv;
             if (tid < BV) s_v[tid] = vv;
         }
-    }
+    };
+    if (tid < D) stage_decay(lbar);
     if constexpr (LOG) {
         if constexpr (SCALAR) {
             if (fused && tid < n) s_lam[tid] = lam_i;
@@ -464,6 +486,27 @@ dl_step_kernel(const StepParams p) {
             if (x < ctot) stage(x, pf[m]);
         }
         for (int x = tid + PF * NT; x < ctot; x += NT) stage(x, *chunk_ptr(x));   // long logs
+    }
+    if constexpr (HINTED) {
+        const int nd = __builtin_amdgcn_readfirstlane(n_dev);
+        if (nd != n) {                                  // the host's value is stale: stage n_dev entries
+            __syncthreads();                            // every speculative chunk has landed
+            n = min(max(nd, 0), C);
+            merge = n == C;
+            log_layout();
+            if (tid < D) {
+                float lb = 0.f;
+                if (n > 0) {
+                    if constexpr (SCALAR) lb = lamlog[sh * C + (n - 1)];
+                    if constexpr (PERKEY) lb = lamlog[(sh * C + (n - 1)) * D + tid];
+                }
+                stage_decay(lb);
+            }
+            if constexpr (SCALAR) {
+                if (tid < n) s_lam[tid] = lamlog[sh * C + tid];
+            }
+            for (int x = tid; x < ctot; x += NT) stage(x, *chunk_ptr(x));
+        }
     }
     __syncthreads();
 
@@ -673,7 +716,7 @@ dl_replay_prep_kernel(const StepParams p) {
     const int H_v = p.H_v, C = p.C;
     const int e = unit / H_v, h = unit - e * H_v;
     const int g = h / (H_v / p.H_k);
-    const int slot = p.slots[e];
+    const int slot = (int)(p.slots[e] & kSlotMask);
     const size_t sh = (size_t)slot * H_v + h;
     const size_t gk = (size_t)slot * p.H_k + g;
     const int n = p.nlog[sh * p.NV];                   // every tile of the slot-head holds the same

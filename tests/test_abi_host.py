@@ -84,6 +84,7 @@ def test_value_tile_choices(d, bv, ok):
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_slots", 0, N.DL_ERR_INVALID_ARG),
+    ("num_slots", (1 << 24) + 1, N.DL_ERR_INVALID_ARG),   # slot ids travel in 24 bits
     ("max_batch", 0, N.DL_ERR_INVALID_ARG),
     ("num_v_heads", 3, N.DL_ERR_INVALID_ARG),       # not a multiple of H_k = 2
     ("num_k_heads", 0, N.DL_ERR_INVALID_ARG),
