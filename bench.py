@@ -81,6 +81,8 @@ def parse(argv=None):
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--distinct-steps", type=int, default=0,
                     help="distinct input steps staged per workload (0 = min(steps, 4 cycles))")
+    ap.add_argument("--windows", default="2:16,2:64,2:256,g128:16,g128:64",
+                    help="comma list of workload:W window measurements ('' = none)")
     ap.add_argument("--sweep", choices=["merge", "state", "split"], default=None,
                     help="merge-interval, state-size or split-replay sweep instead of the headline line")
     return ap.parse_args(argv)
@@ -289,6 +291,69 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
         return out
     finally:
         st.close()
+        torch.cuda.empty_cache()
+
+
+def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4):
+    """W steps of the workload's first batch of slots in one window launch per
+    pool, rotating over `rotate` pools (cold cache when their bytes exceed the
+    Infinity Cache).  The timed region is one graph replay of `reps` launches
+    per pool, after an untimed replay; inputs are device resident."""
+    from linear_attention_recurrent_dl_amd import traffic
+    from workloads import Workload
+    wl = Workload(cfg)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    st, it = tdt[cfg.state_dtype], tdt[cfg.in_dtype]
+    pools = [dl.DeltaLogPool(cfg.num_slots, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update,
+                             cfg.state_dtype, cfg.in_dtype, max_batch=cfg.batch) for _ in range(rotate)]
+    try:
+        for lo in range(0, cfg.num_slots, cfg.batch):
+            ids = np.arange(lo, min(cfg.num_slots, lo + cfg.batch), dtype=np.int32)
+            init = torch.from_numpy(wl.init_base(ids)).to("cuda").to(st).contiguous()
+            for p in pools:
+                p.assign(ids, init)
+            del init
+        steps = wl.generate(wl.main_steps(W))
+        ids = np.ascontiguousarray(steps[0].slot_ids, dtype=np.int32)
+
+        def stack(name, dt):
+            xs = [getattr(s_, name) for s_ in steps]
+            return None if xs[0] is None else torch.from_numpy(np.stack(xs)).to("cuda").to(dt).contiguous()
+
+        q, k, v = stack("q", it), stack("k", it), stack("v", it)
+        lam, beta = stack("lam", torch.float32), stack("beta", torch.float32)
+        out = torch.empty((W, len(ids), cfg.H_v, cfg.d), dtype=torch.float32, device="cuda")
+        for p in pools:                          # first window: empties the logs
+            p.decode_window(ids, W, q, k, v, lam, beta, out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for p in pools:
+                    p.decode_window(ids, W, q, k, v, lam, beta, out)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        launches = reps * rotate
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
+                               cfg.in_dtype, cfg.L)
+        bpl = len(ids) * cfg.H_v * traffic.window_head_bytes(sh, W)
+        del g
+        return {"workload": cfg.name, "kernel": "dl_window_kernel", "W": W, "batch": len(ids),
+                "rotated_pools": rotate, "value_tile": pools[0].value_tile,
+                "launch_us": us, "us_per_step": us / W,
+                "head_steps_per_s": len(ids) * cfg.H_v * W / (us * 1e-6),
+                "tokens_per_s": len(ids) * W / (us * 1e-6),
+                "bytes_per_launch": bpl, "GBps": bpl / (us * 1e-6) / 1e9,
+                "frac_of_8TBps": bpl / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    finally:
+        for p in pools:
+            p.close()
         torch.cuda.empty_cache()
 
 
@@ -555,6 +620,20 @@ def main(argv=None) -> int:
                 extras.append(s)
                 print(f"[bench] {json.dumps(s)}", file=sys.stderr, flush=True)
 
+    windows = []
+    for spec in [t for t in a.windows.split(",") if t]:
+        tag, W = spec.split(":")
+        c = extra_cfg(tag)
+        R = 1 if c.batch == 1 else max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, c))))
+        wr = time_window(c, int(W), R, torch, dl, native)
+        step_us = {x["workload"]: x["decode_launch_us"] for x in extras if x["kernel"] == "deltalog"}
+        step_us[cfg.name] = head["decode_launch_us"]
+        if c.name in step_us:
+            wr["decode_step_us"] = step_us[c.name]
+            wr["speedup_per_step_vs_decode"] = step_us[c.name] / wr["us_per_step"]
+        windows.append(wr)
+        print(f"[bench] window {json.dumps(wr)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(cfg, a.cpu_seconds)
@@ -601,6 +680,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "eager_baseline": eager_head,
         "workloads": extras,
+        "windows": windows,
         "stream_reference": stream_ref,
         "kernel_source_hash": kernel_source_hash(),
     }

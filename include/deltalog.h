@@ -192,6 +192,29 @@ int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
                    const void *q, const void *a_or_k, const void *b_or_v,
                    const float *lambda, const float *beta, float *out, void *stream);
 
+/* W consecutive decode steps of the same B slots in one launch, with the
+ * state held on chip across them ([DL] Eq. 3 applied W times; [FPGA]'s
+ * persistent on-chip state with streamed per-token inputs).  Each (slot,
+ * v-head, value tile) block materializes its tile of the logical state once
+ * ([DL] logical-state equation), keeps it in registers through the W steps and
+ * writes it back once; every slot's log is empty afterwards (as after
+ * dl_merge), whatever its position in the append-merge cycle was.  For use
+ * where the inputs of the W steps exist before the call (a streamed token
+ * sequence, a run of draft tokens).
+ *   slot_ids  host int32 [B], distinct, in range (B == 0 is a no-op)
+ *   W         steps, 1 <= W <= 4096
+ *   q, a_or_k device [W, B, H_k, d_k]   in_dtype, step-major
+ *   b_or_v    device [W, B, H_v, d_v]   in_dtype
+ *   lambda    device fp32 [W, B, H_v] or [W, B, H_v, d_k]; NULL for DL_DECAY_NONE
+ *   beta      device fp32 [W, B, H_v]; NULL for DL_UPDATE_PLAIN
+ *   out       device fp32 [W, B, H_v, d_v]   o of every step
+ * Outputs equal those of W dl_decode_step calls on the same inputs, up to
+ * rounding; the dense state is rounded to state_dtype once, at the end.
+ * Errors as dl_decode_step, plus DL_ERR_INVALID_ARG for W out of range. */
+int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t W,
+                     const void *q, const void *a_or_k, const void *b_or_v,
+                     const float *lambda, const float *beta, float *out, void *stream);
+
 /* Eager read-modify-write baseline of the same step ([DL]'s "state-update
  * tax": read the dense state, transform it, add the outer product, write it
  * back, every token).  Same arguments as dl_decode_step; the pool must have

@@ -19,7 +19,7 @@ from . import _native as N
 from ._native import DeltaLogError, DL_DECAY, DL_DTYPE, DL_UPDATE  # noqa: F401
 
 __all__ = ["dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
-           "dl_decode_step", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
+           "dl_decode_step", "dl_decode_window", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
            "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error", "dl_launch_slot_limit",
            "make_desc", "DeltaLogPool", "DeltaLogError"]
 
@@ -68,6 +68,12 @@ def dl_decode_step(pool: int, slot_ids, q, a_or_k, b_or_v, lam, beta, out, strea
     ids = _ids(slot_ids)
     N.check(N.lib().dl_decode_step(pool, len(ids), _i32p(ids), N.ptr(q), N.ptr(a_or_k), N.ptr(b_or_v),
                                    N.ptr(lam), N.ptr(beta), N.ptr(out), stream), "dl_decode_step")
+
+
+def dl_decode_window(pool: int, slot_ids, W: int, q, a_or_k, b_or_v, lam, beta, out, stream) -> None:
+    ids = _ids(slot_ids)
+    N.check(N.lib().dl_decode_window(pool, len(ids), _i32p(ids), int(W), N.ptr(q), N.ptr(a_or_k), N.ptr(b_or_v),
+                                     N.ptr(lam), N.ptr(beta), N.ptr(out), stream), "dl_decode_window")
 
 
 def dl_eager_step(pool: int, slot_ids, q, a_or_k, b_or_v, lam, beta, out, stream) -> None:
@@ -208,30 +214,39 @@ class DeltaLogPool:
             self._check(init, (len(ids), self.H_v, self.d, self.d), self._tdtype(self.state_dtype), "init")
         dl_slot_assign(self.handle, ids, init, self._stream())
 
-    def _token_args(self, ids, q, a_or_k, b_or_v, lam, beta, out):
-        B = len(ids)
+    def _token_args(self, ids, q, a_or_k, b_or_v, lam, beta, out, W=None):
+        lead = (len(ids),) if W is None else (int(W), len(ids))     # [B, ..] or step-major [W, B, ..]
         if self.device is None:
             return q, a_or_k, b_or_v, lam, beta, out
         it = self._tdtype(self.in_dtype)
         f32 = self._torch.float32
-        self._check(q, (B, self.H_k, self.d), it, "q")
-        self._check(a_or_k, (B, self.H_k, self.d), it, "a_or_k")
-        self._check(b_or_v, (B, self.H_v, self.d), it, "b_or_v")
+        self._check(q, lead + (self.H_k, self.d), it, "q")
+        self._check(a_or_k, lead + (self.H_k, self.d), it, "a_or_k")
+        self._check(b_or_v, lead + (self.H_v, self.d), it, "b_or_v")
         if self.decay == "scalar":
-            self._check(lam, (B, self.H_v), f32, "lambda")
+            self._check(lam, lead + (self.H_v,), f32, "lambda")
         elif self.decay == "per_key":
-            self._check(lam, (B, self.H_v, self.d), f32, "lambda")
+            self._check(lam, lead + (self.H_v, self.d), f32, "lambda")
         if self.update == "delta":
-            self._check(beta, (B, self.H_v), f32, "beta")
+            self._check(beta, lead + (self.H_v,), f32, "beta")
         if out is None:
-            out = self._torch.empty((B, self.H_v, self.d), dtype=f32, device=q.device)
-        self._check(out, (B, self.H_v, self.d), f32, "out")
+            out = self._torch.empty(lead + (self.H_v, self.d), dtype=f32, device=q.device)
+        self._check(out, lead + (self.H_v, self.d), f32, "out")
         return q, a_or_k, b_or_v, lam, beta, out
 
     def decode_step(self, slot_ids, q=None, a_or_k=None, b_or_v=None, lam=None, beta=None, out=None):
         ids = _ids(slot_ids)
         q, a_or_k, b_or_v, lam, beta, out = self._token_args(ids, q, a_or_k, b_or_v, lam, beta, out)
         dl_decode_step(self.handle, ids, q, a_or_k, b_or_v, lam, beta, out, self._stream())
+        return out
+
+    def decode_window(self, slot_ids, W: int, q=None, a_or_k=None, b_or_v=None, lam=None, beta=None, out=None):
+        """W consecutive steps of the same slots in one launch; token tensors
+        are step-major [W, B, ..] and out is [W, B, H_v, d].  Every slot's log
+        is empty afterwards."""
+        ids = _ids(slot_ids)
+        q, a_or_k, b_or_v, lam, beta, out = self._token_args(ids, q, a_or_k, b_or_v, lam, beta, out, W)
+        dl_decode_window(self.handle, ids, W, q, a_or_k, b_or_v, lam, beta, out, self._stream())
         return out
 
     def eager_step(self, slot_ids, q=None, a_or_k=None, b_or_v=None, lam=None, beta=None, out=None):

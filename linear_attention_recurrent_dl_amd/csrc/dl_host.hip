@@ -25,6 +25,8 @@
 namespace dl {
 template <int D, int BV>
 hipError_t launch_step_d(int, int, int, int, int, const StepParams &, size_t, hipStream_t);
+template <int D, int BV>
+hipError_t launch_window_d(int, int, int, int, const WindowParams &, size_t, hipStream_t);
 }
 
 namespace {
@@ -139,6 +141,16 @@ int launch_step(int D, int BV, int mode, int decay, int update, int st, int it, 
                 hipStream_t s) {
 #define DL_TILE(d_, bv_) \
     if (D == d_ && BV == bv_) return (int)launch_step_d<d_, bv_>(mode, decay, update, st, it, p, shmem, s);
+    DL_TILE(128, 128) DL_TILE(128, 64) DL_TILE(128, 32) DL_TILE(128, 16)
+    DL_TILE(64, 64) DL_TILE(64, 32) DL_TILE(32, 32) DL_TILE(16, 16)
+#undef DL_TILE
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_window(int D, int BV, int decay, int update, int st, int it, const WindowParams &p, size_t shmem,
+                  hipStream_t s) {
+#define DL_TILE(d_, bv_) \
+    if (D == d_ && BV == bv_) return (int)launch_window_d<d_, bv_>(decay, update, st, it, p, shmem, s);
     DL_TILE(128, 128) DL_TILE(128, 64) DL_TILE(128, 32) DL_TILE(128, 16)
     DL_TILE(64, 64) DL_TILE(64, 32) DL_TILE(32, 32) DL_TILE(16, 16)
 #undef DL_TILE
@@ -379,6 +391,60 @@ int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void
 int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void *q, const void *a_or_k,
                   const void *b_or_v, const float *lambda, const float *beta, float *out, void *stream) {
     return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, true);
+}
+
+int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t W, const void *q,
+                     const void *a_or_k, const void *b_or_v, const float *lambda, const float *beta, float *out,
+                     void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    const dl_pool_desc &d = pool->desc;
+    if (W < 1 || W > dl::kMaxWindow)
+        return fail(DL_ERR_INVALID_ARG, "window length must be in [1, %d] (got %d)", dl::kMaxWindow, W);
+    int rc = check_slots(pool, B, slot_ids);
+    if (rc) return rc;
+    if (d.decay == DL_DECAY_NONE && lambda) return fail(DL_ERR_INVALID_ARG, "lambda must be NULL for DL_DECAY_NONE");
+    if (d.update == DL_UPDATE_PLAIN && beta) return fail(DL_ERR_INVALID_ARG, "beta must be NULL for DL_UPDATE_PLAIN");
+    if (B == 0) return ok();
+    if (!pool->dry) {
+        if (!q || !a_or_k || !b_or_v || !out) return fail(DL_ERR_INVALID_ARG, "NULL q / a_or_k / b_or_v / out");
+        if (d.decay != DL_DECAY_NONE && !lambda) return fail(DL_ERR_INVALID_ARG, "lambda is NULL");
+        if (d.update == DL_UPDATE_DELTA && !beta) return fail(DL_ERR_INVALID_ARG, "beta is NULL");
+        const uintptr_t align = (uintptr_t)q | (uintptr_t)a_or_k | (uintptr_t)b_or_v | (uintptr_t)out;
+        if (align & 15) return fail(DL_ERR_INVALID_ARG, "token buffers must be 16-byte aligned");
+        const int C = d.merge_interval - 1;
+        const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
+        const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
+        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+        dl::WindowParams p;
+        memset(&p, 0, sizeof p);
+        p.base = pool->buf.base;
+        p.klog = pool->buf.klog;
+        p.ulog = pool->buf.ulog;
+        p.lamlog = pool->buf.lamlog;
+        p.nlog = pool->buf.nlog;
+        p.H_v = d.num_v_heads;
+        p.H_k = d.num_k_heads;
+        p.C = C;
+        p.NV = pool->nv;
+        p.W = W;
+        p.B = B;
+        for (int32_t lo = 0; lo < B; lo += dl::kMaxLaunchSlots) {
+            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, B - lo);
+            p.q = static_cast<const char *>(q) + (size_t)lo * Hk * D * s_in;
+            p.k = static_cast<const char *>(a_or_k) + (size_t)lo * Hk * D * s_in;
+            p.v = static_cast<const char *>(b_or_v) + (size_t)lo * Hv * D * s_in;
+            p.lam = lambda ? lambda + (size_t)lo * Hv * lam_w : nullptr;
+            p.beta = beta ? beta + (size_t)lo * Hv : nullptr;
+            p.out = out + (size_t)lo * Hv * D;
+            memcpy(p.slots, slot_ids + lo, cnt * sizeof(int32_t));
+            p.nunits = cnt * d.num_v_heads * pool->nv;
+            const int e = dl::launch_window(d.d_k, pool->bv, d.decay, d.update, d.state_dtype, d.in_dtype, p, shmem,
+                                            (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail((hipError_t)e, "window kernel launch");
+        }
+    }
+    for (int32_t j = 0; j < B; ++j) pool->n[slot_ids[j]] = 0;   // the window leaves every log empty
+    return ok();
 }
 
 int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {

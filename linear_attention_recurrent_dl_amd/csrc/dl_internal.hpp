@@ -56,6 +56,36 @@ struct StepParams {
     uint32_t slots[kMaxLaunchSlots];   // slot words (see kSlotBits)
 };
 
+// Largest number of steps one window call carries.
+constexpr int kMaxWindow = 4096;
+
+// Arguments of the window kernel: W consecutive decode steps of the same
+// slots, the state of each block's tile held in registers from the first step
+// to the last.  Token arrays are step-major, [W][B][..]; the pointers are
+// offset to this launch's first batch entry and B is the call's batch (the
+// stride between steps).
+struct WindowParams {
+    void *base;          // [P, H_v, NV, D, BV]  state dtype, value-tile major
+    const void *klog;    // [P, H_k, C, D]       input dtype
+    const void *ulog;    // [P, H_v, C, D]       fp32 (delta) | input dtype (plain)
+    const float *lamlog; // [P, H_v, C] | [P, H_v, C, D]
+    int32_t *nlog;       // [P, H_v, NV]
+    const void *q;       // [W, B, H_k, D]
+    const void *k;       // [W, B, H_k, D]
+    const void *v;       // [W, B, H_v, D]
+    const float *lam;    // [W, B, H_v] | [W, B, H_v, D]
+    const float *beta;   // [W, B, H_v]
+    float *out;          // [W, B, H_v, D]
+    int32_t H_v;
+    int32_t H_k;
+    int32_t C;           // log capacity L - 1
+    int32_t NV;          // value tiles per slot-head
+    int32_t nunits;      // blocks in this launch = n * H_v * NV
+    int32_t W;           // steps
+    int32_t B;           // entries per step in the token arrays
+    uint32_t slots[kMaxLaunchSlots];   // slot ids
+};
+
 // Arguments of the state-copy kernel (slot assignment and base read-back):
 // whole-slot state copies between the caller's natural layout [n, H_v, D, D]
 // and the pool's value-tile-major base [P, H_v, NV, D, BV].
@@ -109,5 +139,9 @@ int launch_step(int D, int BV, int mode, int decay, int update, int state_dtype,
                 const StepParams &p, size_t shmem, hipStream_t stream);
 
 int launch_copy(const CopyParams &p, hipStream_t stream);
+
+// Launch one window kernel; returns hipError_t as int.
+int launch_window(int D, int BV, int decay, int update, int state_dtype, int in_dtype, const WindowParams &p,
+                  size_t shmem, hipStream_t stream);
 
 }  // namespace dl

@@ -113,3 +113,10 @@ def merge_head_bytes(sh: StepShape, n: int) -> float:
 def assign_head_bytes(sh: StepShape, zero: bool = False) -> float:
     """Fresh-slot assignment: copy (or zero) the base, clear the counter."""
     return (sh.base_bytes if zero else 2 * sh.base_bytes) + 4
+
+
+def window_head_bytes(sh: StepShape, W: int, n: int = 0) -> float:
+    """One (slot, v-head) over a window of W steps held on chip: the base and
+    n live entries read once, the base written once, W steps of token I/O,
+    the counter read and cleared."""
+    return 2 * sh.base_bytes + n * sh.entry_bytes + W * sh.token_io + 8

@@ -258,3 +258,38 @@ def test_merge_sweep_shapes_validate():
                 assert ei.value.code == N.DL_ERR_UNSUPPORTED
             else:
                 assert dl.dl_pool_sizes(desc)[0] == c.num_slots * c.H_v * c.d * c.d * 4
+
+
+def test_decode_window_rules():
+    """dl_decode_window on a host-only pool: argument checks before anything
+    changes, then every windowed slot's log is empty and the others keep theirs."""
+    lib = N.lib()
+    p = _host_pool()                                     # per-key decay, delta, L = 8
+    ids = np.array([0, 1, 2], dtype=np.int32)
+    ip = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    for _ in range(3):
+        p.decode_step([0, 1, 2, 3])
+    before = p.log_len().tolist()
+    assert before == [3, 3, 3, 3, 0, 0, 0, 0]
+    for W in (0, -1, 4097):
+        assert lib.dl_decode_window(p.handle, 3, ip, W, None, None, None, None, None, None, None) \
+            == N.DL_ERR_INVALID_ARG
+    dup = np.array([1, 1], dtype=np.int32)
+    assert lib.dl_decode_window(p.handle, 2, dup.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 4, None, None,
+                                None, None, None, None, None) == N.DL_ERR_DUPLICATE_SLOT
+    big = np.arange(5, dtype=np.int32)
+    assert lib.dl_decode_window(p.handle, 5, big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 4, None, None,
+                                None, None, None, None, None) == N.DL_ERR_BATCH_TOO_LARGE
+    assert p.log_len().tolist() == before                # refused calls change nothing
+    p.decode_window([0, 2], 5)
+    assert p.log_len().tolist() == [0, 3, 0, 3, 0, 0, 0, 0]
+    # the schedule continues from an empty log
+    p.decode_step([0, 1])
+    assert p.log_len().tolist() == [1, 4, 0, 3, 0, 0, 0, 0]
+    # lambda / beta presence follows the operator, as for a step
+    q = _host_pool(decay="none", update="plain")
+    one = np.array([0], dtype=np.int32)
+    op = one.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.dl_decode_window(q.handle, 1, op, 2, None, None, None, 16, None, None, None) == N.DL_ERR_INVALID_ARG
+    assert lib.dl_decode_window(q.handle, 1, op, 2, None, None, None, None, 16, None, None) == N.DL_ERR_INVALID_ARG
+    assert lib.dl_decode_window(q.handle, 0, op, 2, None, None, None, None, None, None, None) == N.DL_OK
