@@ -414,7 +414,7 @@ int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t 
         const int C = d.merge_interval - 1;
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+        const size_t shmem = dl::window_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
         dl::WindowParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;

@@ -124,6 +124,19 @@ inline int default_value_tile(int D, int state_dtype, long long units) {
     if (D >= 64 && units * (D / wide) < 256) return 32;
     return wide;
 }
+// The window kernel stages token inputs in LDS kWindowChunk steps at a time,
+// double buffered: per buffer q, a [K][D], e^{lambda} [K][D] (per-key decay),
+// v [K][BV], then e^{lambda} (scalar), beta and a . q per step.
+constexpr int kWindowChunk = 8;
+inline size_t window_token_floats(int D, int BV, int decay) {
+    return (size_t)kWindowChunk * (2 * D + (decay == DECAY_PER_KEY ? D : 0) + BV + 4);
+}
+inline size_t window_stage_bytes(int D, int BV, int C, int decay, int update, int in_dtype) {
+    const size_t tok = 2 * window_token_floats(D, BV, decay) * sizeof(float);
+    const size_t log = log_stage_bytes(D, BV, C, decay, update, in_dtype);
+    return tok > log ? tok : log;
+}
+
 inline bool value_tile_supported(int D, int BV) {
     switch (D) {
     case 128: return BV == 128 || BV == 64 || BV == 32 || BV == 16;

@@ -15,13 +15,16 @@
 //   1. load the base tile and stage the live log in LDS; materialize the
 //      logical state S = D(l_bar) S_bar + sum_i D(l_bar - Lam_i) K_i U_i^T in
 //      registers (fp32)
-//   2. for each step w (its token staged in LDS, double buffered, the next
-//      step's inputs in flight):
+//   2. token inputs go to LDS kWindowChunk steps at a time (double buffered;
+//      the next chunk's loads are in flight during the current one, and a . q
+//      and e^{lambda} are formed once per step at staging); then per step,
+//      with one barrier:
 //        P = D(lambda_w) S on the thread's rows; y_q = P^T q, y_k = P^T k by
 //        per-thread FMAs, DPP / row-swap sums across the row groups of a wave
-//        and an LDS sum across waves; every thread forms b on its own columns
-//        (delta: b = beta (v - y_k); plain: the given b), updates
-//        S <- P + a b^T and the first row group writes o = y_q + (a . q) b
+//        and an LDS sum across waves (double buffered by step parity); every
+//        thread forms b on its own columns (delta: b = beta (v - y_k); plain:
+//        the given b), updates S <- P + a b^T, and the first row group writes
+//        o = y_q + (a . q) b
 //   3. write the tile back to the base and empty the log (n <- 0)
 #pragma once
 
@@ -41,15 +44,14 @@ dl_window_kernel(const WindowParams p) {
     constexpr int UCH = BV / UV;
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+    constexpr int KC = kWindowChunk;
     static_assert(VEC % 4 == 0, "columns per thread in float4 groups");
+    static_assert(KC >= 2, "a chunk is restaged after its buffer's last reader has passed a barrier");
 
-    __shared__ float s_q[2][D];                     // q of the step (double buffered)
-    __shared__ float s_k[2][D];                     // a (= k) of the step
-    __shared__ float s_g[PERKEY ? 2 : 1][D];        // e^{lambda} per key
-    __shared__ __align__(16) float s_v[2][BV];      // v (or the given b) on this tile's columns
-    __shared__ __align__(16) float s_red[NW][2][BV];
+    __shared__ __align__(16) float s_red[2][NW][2][BV];   // cross-wave partials, by step parity
     __shared__ float s_lam[kMaxLogCap + 1];         // scalar snapshots
-    extern __shared__ float4 s_dyn[];               // the live log as stored
+    // dynamic: the live log as stored (step 1), then the token buffers (step 2)
+    extern __shared__ float4 s_dyn[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -137,120 +139,175 @@ dl_window_kernel(const WindowParams p) {
     }
 
     // ---- 2. the steps
-    float qv = 0.f, kv = 0.f, vv = 0.f, lv = 0.f, ls = 0.f, bs = 0.f;
-    auto load_token = [&](int w) {
-        const size_t ew = (size_t)w * sB + e;           // entry e of step w
-        if (tid < D) {
-            const size_t qo = (ew * p.H_k + g) * D + tid;
-            qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
-            kv = to_f32(reinterpret_cast<const IT *>(p.k)[qo]);
-            if constexpr (PERKEY) lv = p.lam[(ew * H_v + h) * D + tid];
-            if (tid < BV) vv = to_f32(reinterpret_cast<const IT *>(p.v)[(ew * H_v + h) * D + c0 + tid]);
+    // token buffer layout (floats): q [KC][D], a [KC][D], e^{lambda} [KC][D]
+    // (per key), v [KC][BV], e^{lambda} [KC] (scalar), beta [KC], a . q [KC]
+    constexpr int OQ = 0, OK = KC * D, OG = 2 * KC * D, OV = OG + (PERKEY ? KC * D : 0);
+    constexpr int OGS = OV + KC * BV, OB = OGS + KC, OKQ = OB + KC;
+    constexpr int TB = OKQ + 2 * KC;                    // = window_token_floats
+    constexpr int MQ = (KC * D + NT - 1) / NT;          // q / a / lambda elements per thread and chunk
+    constexpr int MV = (KC * BV + NT - 1) / NT;         // v elements per thread and chunk
+    float *tok = reinterpret_cast<float *>(s_dyn);
+    float rq[MQ], rk[MQ], rl[MQ], rv[MV], rs = 0.f, rb = 0.f;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) rq[m] = rk[m] = rl[m] = 0.f;
+#pragma unroll
+    for (int m = 0; m < MV; ++m) rv[m] = 0.f;
+    const int W = p.W;
+    auto load_chunk = [&](int w0) {                     // steps w0 .. w0 + KC - 1 into registers
+        const int cnt = min(KC, W - w0);
+#pragma unroll
+        for (int m = 0; m < MQ; ++m) {
+            const int x = tid + m * NT, j = x / D, r = x - j * D;
+            if (x < KC * D && j < cnt) {
+                const size_t ew = (size_t)(w0 + j) * sB + e;
+                const size_t qo = (ew * p.H_k + g) * D + r;
+                rq[m] = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+                rk[m] = to_f32(reinterpret_cast<const IT *>(p.k)[qo]);
+                if constexpr (PERKEY) rl[m] = p.lam[(ew * H_v + h) * D + r];
+            }
         }
-        if constexpr (SCALAR) ls = p.lam[ew * H_v + h];
-        if constexpr (DELTA) bs = p.beta[ew * H_v + h];
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const int x = tid + m * NT, j = x / BV, c = x - j * BV;
+            if (x < KC * BV && j < cnt)
+                rv[m] = to_f32(reinterpret_cast<const IT *>(p.v)[(((size_t)(w0 + j) * sB + e) * H_v + h) * D + c0 + c]);
+        }
+        if (tid < cnt) {
+            const size_t ew = (size_t)(w0 + tid) * sB + e;
+            if constexpr (SCALAR) rs = p.lam[ew * H_v + h];
+            if constexpr (DELTA) rb = p.beta[ew * H_v + h];
+        }
     };
-    load_token(0);
-    for (int w = 0; w < p.W; ++w) {
-        const int buf = w & 1;
-        if (tid < D) {
-            s_q[buf][tid] = qv;
-            s_k[buf][tid] = kv;
-            if constexpr (PERKEY) s_g[buf][tid] = __expf(lv);
-            if (tid < BV) s_v[buf][tid] = vv;
-        }
-        const float gs = SCALAR ? __expf(ls) : 1.f;
-        const float beta = bs;
-        if (w + 1 < p.W) load_token(w + 1);
-        __syncthreads();
-
-        // P = D(lambda) S on this thread's rows; partial y_q = P^T q, y_k = P^T k
-        float yq[VEC], yk[VEC];
+    auto store_chunk = [&](float *T) {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) yq[c] = yk[c] = 0.f;
-#pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-            const int r = rg + RG * j;
-            if (!G::RAGGED || r < D) {
-                const float gr = PERKEY ? s_g[PERKEY ? buf : 0][r] : gs;
-                const float qr = s_q[buf][r], kr = s_k[buf][r];
-#pragma unroll
-                for (int c = 0; c < VEC; ++c) {
-                    acc[j][c] *= gr;
-                    yq[c] += acc[j][c] * qr;
-                    if constexpr (DELTA) yk[c] += acc[j][c] * kr;
-                }
+        for (int m = 0; m < MQ; ++m) {
+            const int x = tid + m * NT;
+            if (x < KC * D) {
+                T[OQ + x] = rq[m];
+                T[OK + x] = rk[m];
+                if constexpr (PERKEY) T[OG + x] = __expf(rl[m]);
             }
         }
-        // a . q, summed by every wave for itself
-        float pq = 0.f;
-        for (int r = lane; r < D; r += 64) pq += s_q[buf][r] * s_k[buf][r];
-        const float aq = group_sum<64>(pq);
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-            yq[c] = strided_sum<CG>(yq[c]);
-            if constexpr (DELTA) yk[c] = strided_sum<CG>(yk[c]);
+        for (int m = 0; m < MV; ++m) {
+            const int x = tid + m * NT;
+            if (x < KC * BV) T[OV + x] = rv[m];
         }
-        if (lane < CG) {
+        if (tid < KC) {
+            T[OGS + tid] = SCALAR ? __expf(rs) : 1.f;
+            T[OB + tid] = rb;
+        }
+    };
+    load_chunk(0);
+    __syncthreads();                                    // the log is consumed: its LDS takes the tokens
+    store_chunk(tok);
+    __syncthreads();
+    int buf = 0;
+    for (int w0 = 0; w0 < W; w0 += KC) {
+        const int cnt = min(KC, W - w0);
+        const bool more = w0 + KC < W;
+        if (more) load_chunk(w0 + KC);                  // in flight during this chunk
+        float *T = tok + buf * TB;
+        // a . q of the chunk's steps, wave by wave; read after the steps' barriers
+        for (int j = wave; j < cnt; j += NW) {
+            float pq = 0.f;
+            for (int r = lane; r < D; r += 64) pq += T[OQ + j * D + r] * T[OK + j * D + r];
+            pq = group_sum<64>(pq);
+            if (lane == 0) T[OKQ + j] = pq;
+        }
+        for (int j = 0; j < cnt; ++j) {
+            const int par = (w0 + j) & 1;
+            const float *tq = T + OQ + j * D, *tk = T + OK + j * D, *tg = T + OG + j * D;
+            const float gs = T[OGS + j];
+
+            // P = D(lambda) S on this thread's rows; partial y_q = P^T q, y_k = P^T k
+            float yq[VEC], yk[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) yq[c] = yk[c] = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rg + RG * i;
+                if (!G::RAGGED || r < D) {
+                    const float gr = PERKEY ? tg[r] : gs;
+                    const float qr = tq[r], kr = tk[r];
+#pragma unroll
+                    for (int c = 0; c < VEC; ++c) {
+                        acc[i][c] *= gr;
+                        yq[c] += acc[i][c] * qr;
+                        if constexpr (DELTA) yk[c] += acc[i][c] * kr;
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                yq[c] = strided_sum<CG>(yq[c]);
+                if constexpr (DELTA) yk[c] = strided_sum<CG>(yk[c]);
+            }
+            if (lane < CG) {
+#pragma unroll
+                for (int c = 0; c < VEC; c += 4) {
+                    *reinterpret_cast<float4 *>(&s_red[par][wave][0][cg * VEC + c]) =
+                        make_float4(yq[c], yq[c + 1], yq[c + 2], yq[c + 3]);
+                    if constexpr (DELTA)
+                        *reinterpret_cast<float4 *>(&s_red[par][wave][1][cg * VEC + c]) =
+                            make_float4(yk[c], yk[c + 1], yk[c + 2], yk[c + 3]);
+                }
+            }
+            if (more && j == cnt - 1) store_chunk(tok + (buf ^ 1) * TB);   // the next chunk
+            __syncthreads();
+
+            // b on this thread's columns, S <- P + a b^T, o = y_q + (a . q) b
+            const float beta = T[OB + j];
+            float bcol[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; c += 4) {
-                *reinterpret_cast<float4 *>(&s_red[wave][0][cg * VEC + c]) =
-                    make_float4(yq[c], yq[c + 1], yq[c + 2], yq[c + 3]);
-                if constexpr (DELTA)
-                    *reinterpret_cast<float4 *>(&s_red[wave][1][cg * VEC + c]) =
-                        make_float4(yk[c], yk[c + 1], yk[c + 2], yk[c + 3]);
-            }
-        }
-        __syncthreads();
-
-        // b on this thread's columns, S <- P + a b^T, o = y_q + (a . q) b
-        float bcol[VEC];
+                const float4 v4 = *reinterpret_cast<const float4 *>(T + OV + j * BV + cg * VEC + c);
+                if constexpr (DELTA) {
+                    float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int c = 0; c < VEC; c += 4) {
-            const float4 v4 = *reinterpret_cast<const float4 *>(&s_v[buf][cg * VEC + c]);
-            float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (DELTA) {
-#pragma unroll
-                for (int w2 = 0; w2 < NW; ++w2) {
-                    const float4 a = *reinterpret_cast<const float4 *>(&s_red[w2][1][cg * VEC + c]);
-                    Y.x += a.x; Y.y += a.y; Y.z += a.z; Y.w += a.w;
+                    for (int w2 = 0; w2 < NW; ++w2) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&s_red[par][w2][1][cg * VEC + c]);
+                        Y.x += a.x; Y.y += a.y; Y.z += a.z; Y.w += a.w;
+                    }
+                    bcol[c] = beta * (v4.x - Y.x);
+                    bcol[c + 1] = beta * (v4.y - Y.y);
+                    bcol[c + 2] = beta * (v4.z - Y.z);
+                    bcol[c + 3] = beta * (v4.w - Y.w);
+                } else {
+                    bcol[c] = v4.x;
+                    bcol[c + 1] = v4.y;
+                    bcol[c + 2] = v4.z;
+                    bcol[c + 3] = v4.w;
                 }
-                bcol[c] = beta * (v4.x - Y.x);
-                bcol[c + 1] = beta * (v4.y - Y.y);
-                bcol[c + 2] = beta * (v4.z - Y.z);
-                bcol[c + 3] = beta * (v4.w - Y.w);
-            } else {
-                bcol[c] = v4.x;
-                bcol[c + 1] = v4.y;
-                bcol[c + 2] = v4.z;
-                bcol[c + 3] = v4.w;
             }
-        }
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) {
-            const int r = rg + RG * j;
-            if (!G::RAGGED || r < D) {
-                const float kr = s_k[buf][r];
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rg + RG * i;
+                if (!G::RAGGED || r < D) {
+                    const float kr = tk[r];
 #pragma unroll
-                for (int c = 0; c < VEC; ++c) acc[j][c] += kr * bcol[c];
-            }
-        }
-        if (rg == 0) {
-            float *dst = p.out + (((size_t)w * sB + e) * H_v + h) * D + c0 + cg * VEC;
-#pragma unroll
-            for (int c = 0; c < VEC; c += 4) {
-                float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int w2 = 0; w2 < NW; ++w2) {
-                    const float4 a = *reinterpret_cast<const float4 *>(&s_red[w2][0][cg * VEC + c]);
-                    Y.x += a.x; Y.y += a.y; Y.z += a.z; Y.w += a.w;
+                    for (int c = 0; c < VEC; ++c) acc[i][c] += kr * bcol[c];
                 }
-                st16_stream(dst + c, 0,
-                            make_uint4(__float_as_uint(Y.x + aq * bcol[c]), __float_as_uint(Y.y + aq * bcol[c + 1]),
-                                       __float_as_uint(Y.z + aq * bcol[c + 2]),
-                                       __float_as_uint(Y.w + aq * bcol[c + 3])));
+            }
+            if (rg == 0) {
+                const float aq = T[OKQ + j];
+                float *dst = p.out + (((size_t)(w0 + j) * sB + e) * H_v + h) * D + c0 + cg * VEC;
+#pragma unroll
+                for (int c = 0; c < VEC; c += 4) {
+                    float4 Y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int w2 = 0; w2 < NW; ++w2) {
+                        const float4 a = *reinterpret_cast<const float4 *>(&s_red[par][w2][0][cg * VEC + c]);
+                        Y.x += a.x; Y.y += a.y; Y.z += a.z; Y.w += a.w;
+                    }
+                    st16_stream(dst + c, 0,
+                                make_uint4(__float_as_uint(Y.x + aq * bcol[c]), __float_as_uint(Y.y + aq * bcol[c + 1]),
+                                           __float_as_uint(Y.z + aq * bcol[c + 2]),
+                                           __float_as_uint(Y.w + aq * bcol[c + 3])));
+                }
             }
         }
+        buf ^= 1;
     }
 
     // ---- 3. the state back to the base; the log is empty
