@@ -294,11 +294,12 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
         torch.cuda.empty_cache()
 
 
-def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4):
+def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4, graph: bool = True):
     """W steps of the workload's first batch of slots in one window launch per
     pool, rotating over `rotate` pools (cold cache when their bytes exceed the
     Infinity Cache).  The timed region is one graph replay of `reps` launches
-    per pool, after an untimed replay; inputs are device resident."""
+    per pool, after an untimed replay (graph=False: the same launches issued
+    directly, after one untimed round); inputs are device resident."""
     from linear_attention_recurrent_dl_amd import traffic
     from workloads import Workload
     wl = Workload(cfg)
@@ -326,16 +327,23 @@ def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4):
         for p in pools:                          # first window: empties the logs
             p.decode_window(ids, W, q, k, v, lam, beta, out)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+
+        def launches():
             for _ in range(reps):
                 for p in pools:
                     p.decode_window(ids, W, q, k, v, lam, beta, out)
-        g.replay()
+
+        g = None
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launches()
+        run = g.replay if graph else launches
+        run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        g.replay()
+        run()
         e1.record()
         torch.cuda.synchronize()
         launches = reps * rotate
@@ -346,6 +354,7 @@ def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4):
         del g
         return {"workload": cfg.name, "kernel": "dl_window_kernel", "W": W, "batch": len(ids),
                 "rotated_pools": rotate, "value_tile": pools[0].value_tile,
+                "timing": "graph replay" if graph else "direct launches",
                 "launch_us": us, "us_per_step": us / W,
                 "head_steps_per_s": len(ids) * cfg.H_v * W / (us * 1e-6),
                 "tokens_per_s": len(ids) * W / (us * 1e-6),
@@ -625,7 +634,7 @@ def main(argv=None) -> int:
         tag, W = spec.split(":")
         c = extra_cfg(tag)
         R = 1 if c.batch == 1 else max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, c))))
-        wr = time_window(c, int(W), R, torch, dl, native)
+        wr = time_window(c, int(W), R, torch, dl, native, graph=not a.no_graph)
         step_us = {x["workload"]: x["decode_launch_us"] for x in extras if x["kernel"] == "deltalog"}
         step_us[cfg.name] = head["decode_launch_us"]
         if c.name in step_us:
