@@ -7,7 +7,9 @@
  *   dl_c_consumer <dir>        decode on the GPU
  *   dl_c_consumer --dry        host-only pool: bookkeeping only, no GPU needed
  *
- * <dir>/desc.txt   "P B H_v H_k d L decay update steps value_tile replay_split"
+ * <dir>/desc.txt   "P B H_v H_k d L decay update steps value_tile replay_split [window]"
+ *                  (window W > 0: the last W steps go through one dl_decode_window call;
+ *                  every step must then decode the same slots)
  * <dir>/init.bin   fp32 [P, H_v, d, d] initial states (natural layout)
  * <dir>/ids.bin    int32 [steps, B] slot ids per step
  * <dir>/q.bin, k.bin  fp32 [steps, B, H_k, d];  v.bin fp32 [steps, B, H_v, d]
@@ -121,7 +123,7 @@ int main(int argc, char **argv) {
         return 1;
     }
     const char *dir = argv[1];
-    int P, B, Hv, Hk, D, L, decay, update, steps, value_tile, split;
+    int P, B, Hv, Hk, D, L, decay, update, steps, value_tile, split, window = 0;
     {
         char path[4096];
         snprintf(path, sizeof path, "%s/desc.txt", dir);
@@ -131,7 +133,12 @@ int main(int argc, char **argv) {
             fprintf(stderr, "bad %s\n", path);
             return 4;
         }
+        if (fscanf(f, "%d", &window) != 1) window = 0;
         fclose(f);
+        if (window < 0 || window > steps) {
+            fprintf(stderr, "window %d outside [0, %d]\n", window, steps);
+            return 4;
+        }
     }
     dl_pool_desc d;
     memset(&d, 0, sizeof d);
@@ -188,10 +195,17 @@ int main(int argc, char **argv) {
     float *d_beta = (float *)dev_copy(beta, (size_t)steps * B * Hv * 4);
     float *d_out = NULL;
     CHECK_HIP(hipMalloc((void **)&d_out, (size_t)steps * B * Hv * D * 4));
-    for (int t = 0; t < steps; ++t) {
+    const int nstep = steps - window;
+    for (int t = 0; t < nstep; ++t) {
         CHECK_DL(dl_decode_step(pool, B, ids + (size_t)t * B, d_q + (size_t)t * B * Hk * D, d_k + (size_t)t * B * Hk * D,
                                 d_v + (size_t)t * B * Hv * D, d_lam ? d_lam + (size_t)t * B * Hv * lam_w : NULL,
                                 d_beta ? d_beta + (size_t)t * B * Hv : NULL, d_out + (size_t)t * B * Hv * D, NULL));
+    }
+    if (window > 0) {   /* the remaining steps' inputs and outputs are contiguous, step-major */
+        const size_t t = (size_t)nstep;
+        CHECK_DL(dl_decode_window(pool, B, ids + t * B, window, d_q + t * B * Hk * D, d_k + t * B * Hk * D,
+                                  d_v + t * B * Hv * D, d_lam ? d_lam + t * B * Hv * lam_w : NULL,
+                                  d_beta ? d_beta + t * B * Hv : NULL, d_out + t * B * Hv * D, NULL));
     }
     int32_t *n = (int32_t *)malloc((size_t)P * 4);
     CHECK_DL(dl_get_log_len(pool, n));

@@ -39,7 +39,7 @@ def test_c_consumer_host_only_schedule():
     assert rows == want
 
 
-def _write(dirpath, cfg, value_tile=0, split=0):
+def _write(dirpath, cfg, value_tile=0, split=0, window=0):
     wl = Workload(cfg)
     ids_all = np.arange(cfg.num_slots, dtype=np.int32)
     init = wl.init_base(ids_all).astype(np.float32)
@@ -48,7 +48,7 @@ def _write(dirpath, cfg, value_tile=0, split=0):
     update = {"plain": 0, "delta": 1}[cfg.update]
     with open(os.path.join(dirpath, "desc.txt"), "w") as f:
         f.write(f"{cfg.num_slots} {cfg.batch} {cfg.H_v} {cfg.H_k} {cfg.d} {cfg.L} {decay} {update} "
-                f"{len(steps)} {value_tile} {split}\n")
+                f"{len(steps)} {value_tile} {split} {window}\n")
     init.tofile(os.path.join(dirpath, "init.bin"))
     np.stack([s.slot_ids for s in steps]).astype(np.int32).tofile(os.path.join(dirpath, "ids.bin"))
     for name in ("q", "k", "v"):
@@ -61,13 +61,14 @@ def _write(dirpath, cfg, value_tile=0, split=0):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("base_idx,value_tile,split", [(2, 32, 0), (2, 32, 1), (4, 64, 0), (1, 0, 0)])
-def test_c_consumer_matches_oracle(tmp_path, base_idx, value_tile, split):
+@pytest.mark.parametrize("base_idx,value_tile,split,window", [(2, 32, 0, 0), (2, 32, 1, 0), (4, 64, 0, 0), (1, 0, 0, 0),
+                                                              (2, 32, 0, 9), (4, 64, 0, 23)])
+def test_c_consumer_matches_oracle(tmp_path, base_idx, value_tile, split, window):
     base = CONFIGS[base_idx]
     cfg = small_variant(base, batch=3, steps=23, L=5, H_v=4, H_k=2 if base.H_k < base.H_v else 4,
                         in_dtype="f32", state_dtype="f32", name=f"c_abi_{base.name}")
-    init, steps = _write(str(tmp_path), cfg, value_tile, split)
-    print(f"[gpu] C consumer on {cfg.describe()} value_tile={value_tile} split={split}", flush=True)
+    init, steps = _write(str(tmp_path), cfg, value_tile, split, window)
+    print(f"[gpu] C consumer on {cfg.describe()} value_tile={value_tile} split={split} window={window}", flush=True)
     r = subprocess.run([_binary(), str(tmp_path)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     B, Hv, D, P = cfg.batch, cfg.H_v, cfg.d, cfg.num_slots
@@ -78,8 +79,11 @@ def test_c_consumer_matches_oracle(tmp_path, base_idx, value_tile, split):
     err = RelL2()
     for t, s in enumerate(steps):
         sel, o_ref = E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
-        cnt.decode(s.slot_ids)
+        if t < len(steps) - window:
+            cnt.decode(s.slot_ids)
         err.add(out[t][sel], o_ref)
+    if window:
+        cnt.reset(steps[-1].slot_ids)          # a window leaves the log empty
     st = RelL2()
     st.add(state, E.states())
     assert err.count == len(steps) * B * Hv * D

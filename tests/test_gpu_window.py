@@ -139,3 +139,56 @@ def test_window_headline_shape():
     """GDN, 32 v-heads / 16 q/k heads, d = 128, fp32, batch 1, L = 16: one window of 16 steps."""
     cfg = small_variant(CONFIGS[2], steps=48, name="window_gdn_b1_h32_d128")
     run_window_case(cfg, 16, pre=7)
+
+
+@pytest.mark.parametrize("idx", [2, 4, 5])
+def test_window_graph_replay(idx):
+    """A window launch captured in a HIP graph and replayed three times, with
+    eager device work between replays: each replay applies the same W steps to
+    the state the previous one left, and every output matches the oracle."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    cfg = _small(idx, ragged_fill=False)
+    wl = Workload(cfg)
+    P, Hv, D, W = cfg.num_slots, cfg.H_v, cfg.d, 7
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    pool = dl.DeltaLogPool(P, Hv, cfg.H_k, D, cfg.L, cfg.decay, cfg.update, cfg.state_dtype, cfg.in_dtype,
+                           max_batch=P)
+    ids_all = np.arange(P, dtype=np.int32)
+    pool.assign(ids_all, to_dev(wl.init_base(ids_all), st))
+    E = EagerPool(ids_all, Hv, D, D, cfg.decay, cfg.update, init=wl.init_base(ids_all))
+    win = [wl.step_inputs(d) for d in wl.main_steps(W)]
+    ids = win[0].slot_ids
+    q, k, v = (_stack(win, x) for x in ("q", "k", "v"))
+    lam, beta = _stack(win, "lam"), _stack(win, "beta")
+    dq, dk, dv = to_dev(q, it), to_dev(k, it), to_dev(v, it)
+    dlam, dbeta = to_dev(lam, torch.float32), to_dev(beta, torch.float32)
+    out = torch.empty((W, len(ids), Hv, D), dtype=torch.float32, device="cuda")
+    say(f"[gpu] window graph replay {cfg.describe()} W={W}")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pool.decode_window(ids, W, dq, dk, dv, dlam, dbeta, out)
+    scratch = torch.randn(1 << 20, device="cuda")
+    tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        err = RelL2()
+        for w in range(W):
+            _, o_ref = E.step(ids, q[w], k[w], v[w], None if lam is None else lam[w],
+                              None if beta is None else beta[w])
+            err.add(out[w].cpu().numpy(), o_ref)
+        scratch.mul_(0.5).add_(1.0)
+        torch.cuda.synchronize()
+        say(f"[gpu]   replay {rep}: out rel-L2 {err.value:.3e}")
+        assert err.value <= tol
+        assert np.all(pool.device_log_len()[ids] == 0)
+    st_e = RelL2()
+    st_e.add(pool.read_base(ids_all).float().cpu().numpy(), E.states())
+    assert st_e.value <= tol
+    pool.close()
