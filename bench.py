@@ -9,7 +9,9 @@ slot assignments, then the decode).  The headline workload is the 32-v-head
 d = 128 GDN decode at batch 1 (fp32 state, merge interval 16).  Inputs are the
 seeded synthetic ones from ``workloads`` and sit in device memory before the
 timed region; W untimed steps precede exactly K timed ones, bracketed by
-device synchronization.  Prints one JSON line.
+device synchronization.  In graph mode the K steps are one captured graph,
+replayed once untimed and then five times, each replay timed on its own; the
+median replay is reported (all five are in the line).  Prints one JSON line.
 
 ``roofline`` describes the decode kernel: algorithmic bytes per launch (the
 traffic model in ``linear_attention_recurrent_dl_amd.traffic`` summed over the
@@ -232,12 +234,12 @@ def cycle_steps(rotate: int, L: int, at_least: int) -> int:
 
 
 def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native, value_tile=0, graph=True,
-                  replay_split=False):
+                  replay_split=False, reps=5):
     """Launch mode: W warm-up steps, then K steps each bracketed by a HIP event
     pair on the launch stream.  Graph mode: the next K steps captured once in a
     HIP graph (the kernels read the live-log lengths on the device, so the
-    capture stays valid for every replay), replayed once untimed and once timed
-    by an event pair around the replay."""
+    capture stays valid for every replay), replayed once untimed, then `reps`
+    times, each timed by an event pair around the replay; the median counts."""
     st = Staged(cfg, eager, rotate, distinct, torch, dl, native, value_tile, replay_split)
     try:
         st.plan_bytes(0, warmup)                 # advance the shadow schedule past warm-up
@@ -265,14 +267,18 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
             st.plan_bytes(t0, S)                 # the warm-up replay
             g.replay()
             torch.cuda.synchronize()
-            gb_dec, gb_asg = st.plan_bytes(t0, S)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            out["graph"] = dict(ms=e0.elapsed_time(e1), steps=S, dec_bytes=gb_dec, asg_bytes=gb_asg)
+            times = []
+            for _ in range(max(1, reps)):
+                gb_dec, gb_asg = st.plan_bytes(t0, S)    # every replay covers the same whole cycles
+                torch.cuda.synchronize()
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            out["graph"] = dict(ms=float(np.median(times)), replay_ms=times, steps=S, dec_bytes=gb_dec,
+                                asg_bytes=gb_asg)
             del g
             if gb_asg > 0:
                 # the same steps' assignments alone: their replay time is taken
@@ -282,11 +288,14 @@ def time_workload(cfg, eager, steps, warmup, rotate, distinct, torch, dl, native
                     st.run(t0, S, decode=False)
                 ga.replay()
                 torch.cuda.synchronize()
-                e0.record()
-                ga.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                out["graph"]["assign_ms"] = e0.elapsed_time(e1)
+                atimes = []
+                for _ in range(max(1, reps)):
+                    e0.record()
+                    ga.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    atimes.append(e0.elapsed_time(e1))
+                out["graph"]["assign_ms"] = float(np.median(atimes))
                 del ga
         return out
     finally:
@@ -299,7 +308,8 @@ def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4, graph: bool = 
     pool, rotating over `rotate` pools (cold cache when their bytes exceed the
     Infinity Cache).  The timed region is one graph replay of `reps` launches
     per pool, after an untimed replay (graph=False: the same launches issued
-    directly, after one untimed round); inputs are device resident."""
+    directly, after one untimed round), median of three timed rounds; inputs
+    are device resident."""
     from linear_attention_recurrent_dl_amd import traffic
     from workloads import Workload
     wl = Workload(cfg)
@@ -342,12 +352,15 @@ def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4, graph: bool = 
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        run()
-        e1.record()
-        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
         launches = reps * rotate
-        us = e0.elapsed_time(e1) * 1e3 / launches
+        us = float(np.median(times)) * 1e3 / launches
         sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
                                cfg.in_dtype, cfg.L)
         bpl = len(ids) * cfg.H_v * traffic.window_head_bytes(sh, W)
@@ -393,6 +406,7 @@ def summarize(cfg, r, steps, tag):
         ms_step = gr["ms"] / gr["steps"]
         res.update({
             "ms_per_step": ms_step,
+            "graph_replays_ms": [round(x, 5) for x in gr["replay_ms"]],
             "head_steps_per_s": cfg.batch * cfg.H_v * gr["steps"] / (gr["ms"] * 1e-3),
             "tokens_per_s": cfg.batch * gr["steps"] / (gr["ms"] * 1e-3),
         })
