@@ -17,8 +17,9 @@ median replay is reported (all five are in the line).  Prints one JSON line.
 traffic model in ``linear_attention_recurrent_dl_amd.traffic`` summed over the
 entries of each launch with their actual live-log lengths) divided by the
 average launch duration, measured with HIP events recorded on the stream the
-kernel runs on.  ``workloads`` repeats the measurement for the batch >= 64
-workloads and the eager baseline; there, several independent pools (layers)
+kernel runs on.  ``workloads`` repeats the measurement for the plain
+linear-attention workload (batch 1, d = 16: latency only), the batch >= 64
+workloads and the eager baseline; at batch >= 64 several independent pools (layers)
 are decoded in rotation so that the working set exceeds the 256 MB Infinity
 Cache and the bytes come from HBM.  ``cpu_baseline`` times the fp64 oracle on
 the host on a bounded sample of the headline workload.
@@ -69,7 +70,7 @@ def parse(argv=None):
     ap.add_argument("--value-tile", type=int, default=0,
                     help="value-tile width B_V for the headline pools (0 = library default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
-    ap.add_argument("--extra", default="3,4,5,g64,g128,g256,g512",
+    ap.add_argument("--extra", default="1,3,4,5,g64,g128,g256,g512",
                     help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
     ap.add_argument("--extra-steps", type=int, default=0,
                     help="timed steps per extra workload (0 = whole merge cycles of every rotated pool, at least 4 L)")
@@ -631,7 +632,8 @@ def main(argv=None) -> int:
             from linear_attention_recurrent_dl_amd import traffic
             ws = sum(dl.dl_pool_sizes(dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, c.L, c.decay,
                                                    c.update, c.state_dtype, c.in_dtype)))
-            R = max(1, int(np.ceil(a.rotate_bytes / ws)))
+            # batch-1 workloads are latency-bound with a state of a few KiB: no rotation
+            R = 1 if c.batch == 1 else max(1, int(np.ceil(a.rotate_bytes / ws)))
             xs = a.extra_steps or cycle_steps(R, c.L, 4 * c.L)
             for eager in ([False] if a.no_eager else [False, True]):
                 rr = time_workload(c, eager, xs, c.L, R, min(4 * c.L, xs + c.L), torch, dl, native,
