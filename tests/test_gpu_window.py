@@ -22,7 +22,7 @@ def _stack(inputs, name):
     return None if xs[0] is None else np.stack(xs)
 
 
-def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None):
+def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None, track=None):
     import torch
 
     import linear_attention_recurrent_dl_amd as dl
@@ -36,7 +36,8 @@ def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None):
                            max_batch=max(cfg.batch, P), value_tile=value_tile)
     ids_all = np.arange(P, dtype=np.int32)
     pool.assign(ids_all, to_dev(wl.init_base(ids_all), st))
-    E = EagerPool(ids_all, Hv, D, D, cfg.decay, cfg.update, init=wl.init_base(ids_all))
+    tracked = ids_all if track is None else np.asarray(sorted(track), dtype=np.int32)
+    E = EagerPool(tracked, Hv, D, D, cfg.decay, cfg.update, init=wl.init_base(tracked))
     cnt = schedule.Counters(P, cfg.L)
     descs = wl.plan()
     pre = len(wl.fill_steps()) + (cfg.L // 2 if pre is None else pre)
@@ -48,9 +49,10 @@ def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None):
         nonlocal n_out
         out = pool.decode_step(inp.slot_ids, to_dev(inp.q, it), to_dev(inp.k, it), to_dev(inp.v, it),
                                to_dev(inp.lam, torch.float32), to_dev(inp.beta, torch.float32))
-        _, o_ref = E.step(inp.slot_ids, inp.q, inp.k, inp.v, inp.lam, inp.beta)
+        sel, o_ref = E.step(inp.slot_ids, inp.q, inp.k, inp.v, inp.lam, inp.beta)
         cnt.decode(inp.slot_ids)
-        out_e.add(out.cpu().numpy(), o_ref)
+        if len(sel):
+            out_e.add(out.cpu().numpy()[sel], o_ref)
         n_out += out.numel()
 
     inputs = [wl.step_inputs(d) for d in descs[: pre + W + post]]
@@ -69,8 +71,8 @@ def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None):
                              to_dev(beta, torch.float32))
     win_e = RelL2()
     for w in range(W):
-        _, o_ref = E.step(ids, q[w], k[w], v[w], None if lam is None else lam[w], None if beta is None else beta[w])
-        win_e.add(out[w].cpu().numpy(), o_ref)
+        sel, o_ref = E.step(ids, q[w], k[w], v[w], None if lam is None else lam[w], None if beta is None else beta[w])
+        win_e.add(out[w].cpu().numpy()[sel], o_ref)
     cnt.reset(ids)
     torch.cuda.synchronize()
     dev_n = pool.device_log_len()
@@ -80,14 +82,14 @@ def run_window_case(cfg, W, value_tile=0, pre=None, post=3, window_slots=None):
     pool.flush_all()
     torch.cuda.synchronize()
     st_e = RelL2()
-    st_e.add(pool.read_base(ids_all).float().cpu().numpy(), E.states())
+    st_e.add(pool.read_base(tracked).float().cpu().numpy(), E.states())
     counter_mismatch += int(np.sum(pool.device_log_len() != 0))
     say(f"[gpu]   window out rel-L2 {win_e.value:.3e} over {win_e.count} values; steps {out_e.value:.3e}; "
         f"state {st_e.value:.3e}; live lengths before {sorted(set(n_before[ids].tolist()))}; "
         f"counter mismatch {counter_mismatch}")
     pool.close()
     tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
-    assert win_e.count == W * B * Hv * D
+    assert win_e.count == W * int(np.isin(ids, tracked).sum()) * Hv * D
     assert win_e.value <= tol and out_e.value <= tol and st_e.value <= tol, (win_e.value, out_e.value, st_e.value)
     assert counter_mismatch == 0
     return n_before[ids]
@@ -192,3 +194,12 @@ def test_window_graph_replay(idx):
     st_e.add(pool.read_base(ids_all).float().cpu().numpy(), E.states())
     assert st_e.value <= tol
     pool.close()
+
+
+def test_window_full_size_sampled():
+    """The benchmark's batch window: GDN, batch 128, 32 v-heads, d = 128, fp32,
+    default value tiles, W = 64, after a few steps of every slot; three slots
+    followed by the oracle."""
+    from workloads import headline_gdn
+    cfg = headline_gdn(128, steps=80)
+    run_window_case(cfg, 64, pre=5, post=3, track=[0, 77, 127])
