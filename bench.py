@@ -70,7 +70,7 @@ def parse(argv=None):
     ap.add_argument("--value-tile", type=int, default=0,
                     help="value-tile width B_V for the headline pools (0 = library default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch >= 64 workloads")
-    ap.add_argument("--extra", default="1,3,4,5,g64,g128,g256,g512",
+    ap.add_argument("--extra", default="1,3,4,5,5tp8,g64,g128,g256,g512",
                     help="comma list of extra workloads (config index or gB = GDN fp32 at batch B)")
     ap.add_argument("--extra-steps", type=int, default=0,
                     help="timed steps per extra workload (0 = whole merge cycles of every rotated pool, at least 4 L)")
@@ -572,9 +572,17 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
 
 
 def extra_cfg(tag: str):
+    """Config index 1-5; gB = GDN fp32 d = 128 at batch B; NtpG = config N's
+    per-GPU share under G-way head sharding (H_v / G v-heads, H_k / G q/k heads)."""
+    import dataclasses
     from workloads import CONFIGS, headline_gdn
     if tag.startswith("g"):
         return headline_gdn(int(tag[1:]))
+    if "tp" in tag:
+        idx, G = (int(x) for x in tag.split("tp"))
+        base = CONFIGS[idx]
+        return dataclasses.replace(base, H_v=base.H_v // G, H_k=max(1, base.H_k // G),
+                                   name=f"{base.name}_tp{G}_share")
     return CONFIGS[int(tag)]
 
 
