@@ -132,8 +132,10 @@ def test_window_from_ragged_logs():
 
 
 def test_window_long_and_chunked_launch():
-    """W = 300 steps, and 520 slots: more entries than one launch carries."""
+    """W = 300 and the largest window, W = 4096; and 520 slots: more entries
+    than one launch carries."""
     run_window_case(_small(1, L=8, steps=320), 300, pre=2, post=2)
+    run_window_case(_small(1, L=8, steps=4104), 4096, pre=2, post=2)
     run_window_case(_small(1, batch=520, num_slots=520, H_v=2, H_k=2, steps=12), 5, pre=2, post=2)
 
 
