@@ -118,10 +118,12 @@ inline size_t log_stage_bytes(int D, int BV, int C, int decay, int update, int i
 // Default value-tile width.  Wide tiles (half the row for an fp32 d = 128
 // state, the whole row otherwise) stream best once a batch fills the GPU with
 // blocks; when max_batch * H_v slot-heads would give fewer blocks than the
-// 256 CUs, 32-column tiles spread one step over more CUs instead.
+// 256 CUs, narrower tiles spread one step over more CUs instead: the widest of
+// 32 or 16 columns that still gives 256 blocks (16 only at d = 128, for 32
+// slot-heads or fewer, where it measured about 2% faster per step).
 inline int default_value_tile(int D, int state_dtype, long long units) {
     const int wide = (D == 128 && state_dtype != BF16) ? 64 : D;
-    if (D >= 64 && units * (D / wide) < 256) return 32;
+    if (D >= 64 && units * (D / wide) < 256) return (D == 128 && units * (D / 32) < 256) ? 16 : 32;
     return wide;
 }
 // The window kernel stages token inputs in LDS kWindowChunk steps at a time,

@@ -58,7 +58,9 @@ def test_pool_sizes_formula():
         lam_w = {"none": 0, "scalar": 1, "per_key": D}[cfg.decay]
         bv = dl.dl_value_tile(desc)
         wide = 64 if (D == 128 and cfg.state_dtype == "f32") else D
-        assert bv == (32 if (D >= 64 and cfg.batch * Hv * (D // wide) < 256) else wide), cfg.name
+        units = cfg.batch * Hv
+        narrow = 16 if (D == 128 and units * (D // 32) < 256) else 32
+        assert bv == (narrow if (D >= 64 and units * (D // wide) < 256) else wide), cfg.name
         assert sz == [P * Hv * D * D * s_st, P * Hk * C * D * s_in, P * Hv * C * D * s_b,
                       P * Hv * C * lam_w * 4, P * Hv * (D // bv) * 4, 0], cfg.name
         # split replay adds one launch's coefficient scratch: 2 L floats per (entry, v-head)
