@@ -3,6 +3,7 @@
     python -m linear_attention_recurrent_dl_amd.rocprof_summary trace  <results.db | kernel_trace.csv>
     python -m linear_attention_recurrent_dl_amd.rocprof_summary pmc    <results.db | counter_collection.csv> COUNTER
     python -m linear_attention_recurrent_dl_amd.rocprof_summary traffic FETCH_DB WRITE_DB KERNEL_SUBSTR COPY_BYTES [OUT.json]
+    python -m linear_attention_recurrent_dl_amd.rocprof_summary tail   <kernel_trace.csv> KERNEL_SUBSTR N
 
 ``trace`` prints count / average / min / max duration per kernel name;
 ``pmc`` prints, per kernel name, the average value of COUNTER per dispatch and
@@ -11,8 +12,12 @@ WRITE_SIZE run into HBM bytes per launch of the kernel whose name contains
 KERNEL_SUBSTR: each counter (KiB per dispatch) is scaled by the factor that
 maps the same counter of a plain device copy of COPY_BYTES bytes (the largest
 copy kernel in the run, which reads and writes COPY_BYTES each) onto its known
-size.  Works on the SQLite database rocprofv3 writes by default
-(``*_results.db``) and on its CSV output.
+size.  ``tail`` splits the dispatches of the kernel whose name contains
+KERNEL_SUBSTR, in start order, into all but the last N and the last N, and
+prints count and average duration of each part and the median start-to-start
+period of the last N (a timed graph replay is the last dispatches of a run).
+Works on the SQLite database rocprofv3 writes by default (``*_results.db``)
+and on its CSV output (``tail``: CSV only).
 """
 
 from __future__ import annotations
@@ -45,6 +50,22 @@ def trace_rows(path: str):
                     agg[name].extend([float(r["AverageNs"])] * int(r["Calls"]))
     rows = [(n, len(v), sum(v) / len(v), min(v), max(v), sum(v)) for n, v in agg.items()]
     return sorted(rows, key=lambda r: -r[5])
+
+
+def trace_tail(path: str, sub: str, n: int):
+    """(count_head, avg_head_ns, count_tail, avg_tail_ns, median_period_tail_ns) of
+    one kernel's dispatches in start order, the tail being the last n."""
+    spans = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if sub in (r.get("Kernel_Name") or ""):
+                spans.append((float(r["Start_Timestamp"]), float(r["End_Timestamp"])))
+    spans.sort()
+    head, tail = spans[:-n] if n < len(spans) else [], spans[-n:]
+    avg = lambda xs: sum(e - s for s, e in xs) / len(xs) if xs else 0.0
+    starts = [s for s, _ in tail]
+    per = sorted(b - a for a, b in zip(starts, starts[1:]))
+    return len(head), avg(head), len(tail), avg(tail), (per[len(per) // 2] if per else 0.0)
 
 
 def pmc_dispatches(path: str, counter: str):
@@ -155,6 +176,11 @@ def main(argv=None) -> int:
         print(f"{'kernel':100s} {'dispatches':>10s} {counter + '/dispatch':>20s}")
         for n, c, v in pmc_rows(path, counter):
             print(f"{_short(n):100s} {c:10d} {v:20.1f}")
+    elif mode == "tail":
+        nh, ah, nt, at, pt = trace_tail(path, argv[2], int(argv[3]))
+        print(f"kernel containing: {argv[2]}")
+        print(f"first {nh} dispatches: avg {ah / 1e3:.3f} us")
+        print(f"last {nt} dispatches: avg {at / 1e3:.3f} us, median start-to-start {pt / 1e3:.3f} us")
     elif mode == "traffic":
         import json
         t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
