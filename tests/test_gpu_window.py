@@ -205,3 +205,10 @@ def test_window_full_size_sampled():
     from workloads import headline_gdn
     cfg = headline_gdn(128, steps=80)
     run_window_case(cfg, 64, pre=5, post=3, track=[0, 77, 127])
+
+
+@pytest.mark.parametrize("idx", [2, 4])
+def test_window_on_eager_pool(idx):
+    """Merge interval 1 (no log; steps run the eager kernel): the window
+    materializes nothing and carries the state through its steps."""
+    run_window_case(_small(idx, L=1), 6, pre=3)
