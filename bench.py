@@ -84,6 +84,8 @@ def parse(argv=None):
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--distinct-steps", type=int, default=0,
                     help="distinct input steps staged per workload (0 = min(steps, 4 cycles))")
+    ap.add_argument("--flush", default="g256,4",
+                    help="comma list of workloads whose full logs dl_flush_all materializes ('' = none)")
     ap.add_argument("--windows", default="2:16,2:64,2:256,g128:16,g128:64",
                     help="comma list of workload:W window measurements ('' = none)")
     ap.add_argument("--sweep", choices=["merge", "state", "split"], default=None,
@@ -380,6 +382,47 @@ def time_window(cfg, W, rotate, torch, dl, native, reps: int = 4, graph: bool = 
         torch.cuda.empty_cache()
 
 
+def time_flush(cfg, rotate, torch, dl, native, reps: int = 5):
+    """dl_flush_all on pools whose every log is full (L - 1 entries): the
+    standalone merge materializes base + log and empties the log.  Each timed
+    round refills the logs with L - 1 untimed decode steps, then one graph
+    replay flushes every pool; median of `reps` rounds."""
+    from linear_attention_recurrent_dl_amd import traffic
+    st = Staged(cfg, False, rotate, cfg.L - 1, torch, dl, native)
+    try:
+        C = cfg.L - 1
+        st.run(0, C * rotate)                     # every slot of every pool holds L - 1 live entries
+        torch.cuda.synchronize()
+        # flush_all picks its slots from the host mirror, which is full here; the
+        # capture empties the mirror while the device logs stay full for the replay
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for p in st.pools:
+                p.flush_all()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for rep in range(reps):
+            if rep:
+                st.run(0, C * rotate)             # refill: mirror and device back to L - 1 entries
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        us = float(np.median(times)) * 1e3 / rotate
+        sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
+                               cfg.in_dtype, cfg.L)
+        bpl = cfg.num_slots * cfg.H_v * traffic.merge_head_bytes(sh, C)
+        return {"workload": cfg.name, "kernel": "dl_step_kernel (standalone merge)", "live_entries": C,
+                "slots": cfg.num_slots, "rotated_pools": rotate, "launch_us": us, "bytes_per_launch": bpl,
+                "GBps": bpl / (us * 1e-6) / 1e9, "frac_of_8TBps": bpl / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                "replays_ms": times}
+    finally:
+        st.close()
+        torch.cuda.empty_cache()
+
+
 def summarize(cfg, r, steps, tag):
     from linear_attention_recurrent_dl_amd import traffic
     sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
@@ -653,6 +696,14 @@ def main(argv=None) -> int:
                 extras.append(s)
                 print(f"[bench] {json.dumps(s)}", file=sys.stderr, flush=True)
 
+    flushes = []
+    for tag in [t for t in a.flush.split(",") if t]:
+        c = extra_cfg(tag)
+        R = max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, c))))
+        fr = time_flush(c, R, torch, dl, native)
+        flushes.append(fr)
+        print(f"[bench] flush {json.dumps(fr)}", file=sys.stderr, flush=True)
+
     windows = []
     for spec in [t for t in a.windows.split(",") if t]:
         tag, W = spec.split(":")
@@ -714,6 +765,7 @@ def main(argv=None) -> int:
         "eager_baseline": eager_head,
         "workloads": extras,
         "windows": windows,
+        "flush": flushes,
         "stream_reference": stream_ref,
         "kernel_source_hash": kernel_source_hash(),
     }
