@@ -423,6 +423,47 @@ def time_flush(cfg, rotate, torch, dl, native, reps: int = 5):
         torch.cuda.empty_cache()
 
 
+def host_call_cost(dl, native, seconds: float = 0.5):
+    """Host-side cost of one dl_decode_step call (validation, duplicate check,
+    live-length mirror; the phase split of every entry), measured on host-only
+    pools, which do everything but enqueue: microseconds per call through the
+    C symbol (ctypes, whose conversion of the ten arguments is included), for
+    batches of 1, 64 and 256 slots."""
+    from workloads import headline_gdn
+    lib = native.lib()
+    out = []
+    for B in (1, 64, 256):
+        c = headline_gdn(B)
+        pool = dl.DeltaLogPool(c.num_slots, c.H_v, c.H_k, c.d, c.L, c.decay, c.update, c.state_dtype,
+                               c.in_dtype, max_batch=B, device=None)
+        ids = np.arange(B, dtype=np.int32)
+        ip = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        f, h = lib.dl_decode_step, pool.handle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            for _ in range(1000):
+                f(h, B, ip, None, None, None, None, None, None, None)
+            n += 1000
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        pool.close()
+        out.append({"batch": B, "us_per_call": el / n * 1e6, "calls": n})
+    # the Python-to-C call itself: a trivial exported function in the same loop
+    g, n, t0 = lib.dl_launch_slot_limit, 0, time.perf_counter()
+    while True:
+        for _ in range(1000):
+            g()
+        n += 1000
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    floor = el / n * 1e6
+    for o in out:
+        o["trivial_call_us"] = floor          # a no-argument exported function, same path
+    return out
+
+
 def summarize(cfg, r, steps, tag):
     from linear_attention_recurrent_dl_amd import traffic
     sh = traffic.StepShape(cfg.H_v, cfg.H_k, cfg.d, cfg.d, cfg.decay, cfg.update, cfg.state_dtype,
@@ -718,6 +759,9 @@ def main(argv=None) -> int:
         windows.append(wr)
         print(f"[bench] window {json.dumps(wr)}", file=sys.stderr, flush=True)
 
+    host_cost = host_call_cost(dl, native)
+    print(f"[bench] host call {json.dumps(host_cost)}", file=sys.stderr, flush=True)
+
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(cfg, a.cpu_seconds)
@@ -766,6 +810,7 @@ def main(argv=None) -> int:
         "workloads": extras,
         "windows": windows,
         "flush": flushes,
+        "host_call": host_cost,
         "stream_reference": stream_ref,
         "kernel_source_hash": kernel_source_hash(),
     }
