@@ -673,7 +673,7 @@ def extra_cfg(tag: str):
 def main(argv=None) -> int:
     a = parse(argv)
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU per process; --gpus must be 1",
                           "requested_gpus": a.gpus}))
         print("bench.py: only --gpus 1 is supported (one GPU per process, no multi-GPU path)",
               file=sys.stderr)
