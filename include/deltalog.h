@@ -73,7 +73,7 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *                   1 <= P <= 2^24
  *   max_batch       largest B of one dl_decode_step / dl_slot_assign / dl_merge
  *   num_v_heads     H_v;  num_k_heads H_k (H_v % H_k == 0; grouped value heads)
- *   d_k, d_v        head dims; this build supports d_k == d_v in {16, 32, 64, 128}
+ *   d_k, d_v        head dims; the library supports d_k == d_v in {16, 32, 64, 128}
  *   merge_interval  L = [DL]'s M: one merge every L decodes of a slot; the log
  *                   holds at most L-1 entries.  1 <= L <= 64.  L == 1 makes the
  *                   pool an eager read-modify-write state (no log).
