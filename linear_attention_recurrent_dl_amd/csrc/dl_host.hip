@@ -252,6 +252,14 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
         const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+        // A launch recorded into a graph may be replayed at any phase of the
+        // append-merge cycle, so it carries no live lengths from the host.
+        bool capturing = true;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess)
+            capturing = cs != hipStreamCaptureStatusNone;
+        else
+            (void)hipGetLastError();            // unknown: take the counter, always correct
         dl::StepParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -275,7 +283,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
             if (mode == dl::MODE_STEP) {         // the host's live lengths ride in the slot words
                 for (int32_t j = 0; j < cnt; ++j)
-                    p.slots[j] |= (uint32_t)pool->n[ids[lo + j]] << dl::kSlotBits;
+                    p.slots[j] |= (capturing ? dl::kNoHint : (uint32_t)pool->n[ids[lo + j]]) << dl::kSlotBits;
             }
             if (split) {
                 // ReplayPrep, one block per (entry, v-head), into the coefficient scratch

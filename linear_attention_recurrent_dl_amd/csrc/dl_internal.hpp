@@ -21,6 +21,9 @@ constexpr int kMaxLogCap = 63;
 constexpr int kSlotBits = 24;
 constexpr uint32_t kSlotMask = (1u << kSlotBits) - 1;
 constexpr int kMaxSlots = 1 << kSlotBits;
+// Top byte of a decode launch's slot word when the host gives no live length
+// (launches recorded into a graph, whose replays may start at any phase).
+constexpr uint32_t kNoHint = 0xFF;
 
 enum Mode : int {
     MODE_STEP = 0,   // DeltaLog decode: append, or merge when the log is full

@@ -334,18 +334,20 @@ dl_step_kernel(const StepParams p) {
     const int cg = tid % CG, rg = tid / CG;
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
-    // Live length n.  A decode launch takes the host's value for the slot (the
-    // slot word's top byte), so that no load below waits for the device
-    // counter; the counter, read alongside, decides (step 2 stages again when
-    // the two differ, as when a captured step is replayed from another phase).
-    // Its index is made opaque to keep it a vector load: a scalar one would
-    // order the scalar argument loads behind it.
+    // Live length n.  A direct decode launch takes the host's value for the
+    // slot (the slot word's top byte), so that no load below waits for the
+    // device counter; the counter, read alongside, decides (step 2 stages
+    // again when the two differ, as after direct launches that follow a
+    // graph capture).  A launch recorded into a graph carries no value and
+    // waits for the counter.  The counter's index is made opaque to keep it a
+    // vector load: a scalar one would order the scalar argument loads behind it.
     int n = 0, n_dev = 0;
     if constexpr (HINTED) {
-        n = min((int)(sword >> kSlotBits), C);
         int ni = (int)(sh * NV + vt);
         asm volatile("" : "+v"(ni));
         n_dev = p.nlog[ni];
+        const uint32_t hint = sword >> kSlotBits;
+        n = hint == kNoHint ? min(max(__builtin_amdgcn_readfirstlane(n_dev), 0), C) : min((int)hint, C);
     } else if constexpr (LOG) {
         n = p.nlog[sh * NV + vt];
     }

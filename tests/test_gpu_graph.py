@@ -69,3 +69,57 @@ def test_graph_replay_matches_oracle(idx, value_tile, split):
         assert err.value <= tol
         assert np.all(n_dev == want_n)
     pool.close()
+
+
+@pytest.mark.parametrize("idx", [2, 4, 5])
+def test_direct_steps_after_a_capture(idx):
+    """Capturing steps advances the host's live lengths but not the device's.
+    Direct steps afterwards carry host values that differ from the device
+    counters, so every block restages its log from the counter; outputs,
+    states and device counters must follow the direct steps alone."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2, schedule
+
+    base = CONFIGS[idx]
+    cfg = small_variant(base, batch=3, steps=14, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
+                        name=f"capture_then_direct_{base.name}", random_slots=False, replace_per_step=0,
+                        ragged_fill=False, num_slots=3)
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    P = cfg.num_slots
+    pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, max_batch=cfg.batch)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    cnt = schedule.Counters(P, cfg.L)
+    steps = [wl.step_inputs(d) for d in wl.main_steps()]
+    dev = [dict(q=to_dev(s.q, it), k=to_dev(s.k, it), v=to_dev(s.v, it), lam=to_dev(s.lam, torch.float32),
+                beta=to_dev(s.beta, torch.float32)) for s in steps]
+    say(f"[gpu] direct steps after a capture: {cfg.describe()}")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):                  # recorded, never replayed
+        for s, d in zip(steps[:3], dev[:3]):
+            pool.decode_step(s.slot_ids, d["q"], d["k"], d["v"], d["lam"], d["beta"])
+    torch.cuda.synchronize()
+    assert np.all(pool.log_len() == 3) and np.all(pool.device_log_len() == 0)
+    err = RelL2()
+    for s, d in zip(steps[3:], dev[3:]):
+        out = pool.decode_step(s.slot_ids, d["q"], d["k"], d["v"], d["lam"], d["beta"])
+        _, o_ref = E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
+        cnt.decode(s.slot_ids)
+        err.add(out.cpu().numpy(), o_ref)
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == cnt.n[:, None])
+    pool.flush_all()
+    st_e = RelL2()
+    st_e.add(pool.read_base(ids).float().cpu().numpy(), E.states())
+    tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
+    say(f"[gpu]   out rel-L2 {err.value:.3e}, state rel-L2 {st_e.value:.3e}")
+    del g
+    pool.close()
+    assert err.value <= tol and st_e.value <= tol
