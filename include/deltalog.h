@@ -187,7 +187,16 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids,
  * A slot whose log holds L-1 entries takes the merge step: its output is
  * computed from base + log + this token, and the base is rewritten with the
  * materialized state; its log becomes empty.  Any other slot appends this
- * token's (a_t, b_t, snapshot) at log index n and leaves the base unchanged. */
+ * token's (a_t, b_t, snapshot) at log index n and leaves the base unchanged.
+ *
+ * Graph capture: a call made while `stream` is capturing records its launches
+ * and advances the host's live lengths as if they had run.  The kernels take
+ * each slot's phase (append or merge, entry index) from the device counters,
+ * so a captured step stays correct when replayed at any point of the cycle;
+ * dl_get_log_len then reflects the calls made, not the replays.  A direct
+ * call also passes the host's live lengths to the kernels, which use them to
+ * start loading the log early and fall back to the device counters when they
+ * differ (as after a capture); captured launches pass none. */
 int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
                    const void *q, const void *a_or_k, const void *b_or_v,
                    const float *lambda, const float *beta, float *out, void *stream);

@@ -14,9 +14,12 @@
 // and decay snapshot, which only the first tile writes (the designated
 // writer).  Per block:
 //
-//   1. issue every load before consuming any: token inputs, the live log as
-//      16-byte chunks, then the base tile (RPT x 16-byte non-temporal loads
-//      per thread over one contiguous run; the base is value-tile major)
+//   1. the live length n: the host's value for the slot in a direct launch,
+//      checked against the device counter (restaged when they differ); the
+//      counter itself in a launch recorded into a graph.  Then every load is
+//      issued before any is consumed: token inputs, the live log as 16-byte
+//      chunks, then the base tile (RPT x 16-byte non-temporal loads per
+//      thread over one contiguous run; the base is value-tile major)
 //   2. l' = l_bar + lambda (l_bar = newest snapshot, or 0 for an empty log);
 //      q~ = e^{l'} * q and k~ = e^{l'} * k go to LDS, the log lands in LDS as
 //      stored
