@@ -524,6 +524,17 @@ def summarize(cfg, r, steps, tag):
     return res
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, seconds: float):
     """fp64 oracle (eager recurrence) on a bounded sample of the workload."""
     import oracle
@@ -553,7 +564,7 @@ def cpu_baseline(cfg, seconds: float):
             "sample": f"{n} steps of {cfg.name} (all {cfg.batch * cfg.H_v} slot-heads each), fp64 NumPy "
                       f"eager recurrence, {wall:.1f} s wall",
             "tokens_per_s": cfg.batch * n / wall, "cpu_seconds": cpu, "blas_threads": blas_threads,
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
 
 
 def stream_reference(torch, mib: int = 1024, reps: int = 10):
