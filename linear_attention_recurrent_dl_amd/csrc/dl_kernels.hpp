@@ -82,6 +82,19 @@ __device__ __forceinline__ void unpack_f32(const uint4 &w, float (&out)[N]) {
     }
 }
 
+// Dot product of two 16-byte vectors of T, in fp32.
+template <typename T>
+__device__ __forceinline__ float dot16(const uint4 &a, const uint4 &b) {
+    constexpr int N = 16 / (int)sizeof(T);
+    float x[N], y[N];
+    unpack_f32<T, N>(a, x);
+    unpack_f32<T, N>(b, y);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += x[j] * y[j];
+    return s;
+}
+
 template <typename T, int N>
 __device__ __forceinline__ uint4 pack_16(const float (&x)[N]) {
     static_assert(N * sizeof(T) == 16, "one 16-byte vector");
@@ -302,6 +315,14 @@ dl_step_kernel(const StepParams p) {
     constexpr bool SPLIT = MODE == MODE_STEP_SPLIT;   // appends read ReplayPrep's coefficients
     constexpr bool STEP = MODE == MODE_STEP || SPLIT;
     constexpr bool HINTED = MODE == MODE_STEP;        // loads follow the host's live length
+    // Scalar or no decay: the replay coefficients' raw dot products are formed
+    // while the log is staged (one key chunk per thread, DPP sums over the
+    // chunk's CPE threads) and weighted e^{l'-Lam_i} where they are read, so
+    // there is no separate coefficient pass or barrier.  Per-key decay needs
+    // the snapshot chunk beside each key chunk and keeps the pass; so do bf16
+    // states, whose kernels the packed q / a chunks would push past 128 VGPRs.
+    constexpr bool FC = (MODE == MODE_STEP || MODE == MODE_EAGER) && DECAY != DECAY_PER_KEY && sizeof(ST) == 4;
+    constexpr int CPE = D / (16 / (int)sizeof(IT));   // 16-byte key chunks per log entry
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
     static_assert(BV % UV == 0, "value-factor chunks");
@@ -387,6 +408,14 @@ dl_step_kernel(const StepParams p) {
     if constexpr (SCALAR && LOG) {
         if (fused && tid < n) lam_i = lamlog[sh * C + tid];
     }
+    // q and a on the KV keys of this thread's key chunks (the same positions
+    // for every chunk it stages), kept packed until used
+    uint4 qpk = make_uint4(0, 0, 0, 0), apk = qpk;
+    if constexpr (FC && TOKEN) {
+        const size_t qo = ((size_t)e * p.H_k + g) * D + (tid % CPE) * (16 / (int)sizeof(IT));
+        qpk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.q) + qo);
+        apk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.k) + qo);
+    }
     // split replay: this append's coefficients from the scratch (c^q, c^k per
     // live entry, then a . q)
     float cq_r = 0.f, ck_r = 0.f, s_r = 0.f;
@@ -434,6 +463,22 @@ dl_step_kernel(const StepParams p) {
     // keep that array in scratch memory)
     auto stage = [&](int x, const uint4 w) {
         *reinterpret_cast<uint4 *>(s_log + (size_t)x * 16) = make_uint4(w.x, w.y, w.z, w.w);
+    };
+    // raw replay dot products of key chunk x (entry x / CPE) with q and a,
+    // completed over the entry's CPE consecutive threads; every thread of the
+    // block calls this for the same chunk block
+    auto chunk_dots = [&](const int x, const uint4 w) {
+        float pq = 0.f, pk = 0.f;
+        if (x < cK) {
+            pq = dot16<IT>(w, qpk);
+            if constexpr (DELTA) pk = dot16<IT>(w, apk);
+        }
+        pq = group_sum<CPE>(pq);
+        if constexpr (DELTA) pk = group_sum<CPE>(pk);
+        if (x < cK && x % CPE == 0) {
+            s_cq[x / CPE] = pq;
+            if constexpr (DELTA) s_ck[x / CPE] = pk;
+        }
     };
     uint4 pf[PF];
     if constexpr (LOG) {
@@ -489,8 +534,29 @@ dl_step_kernel(const StepParams p) {
         for (int m = 0; m < PF; ++m) {
             const int x = tid + m * NT;
             if (x < ctot) stage(x, pf[m]);
+            if constexpr (FC && TOKEN) {
+                if (m * NT < cK) chunk_dots(x, pf[m]);
+            }
         }
-        for (int x = tid + PF * NT; x < ctot; x += NT) stage(x, *chunk_ptr(x));   // long logs
+        if constexpr (FC && TOKEN) {
+            for (int xb = PF * NT; xb < ctot; xb += NT) {   // long logs (uniform trip count: DPP sums inside)
+                const int x = xb + tid;
+                uint4 w = make_uint4(0, 0, 0, 0);
+                if (x < ctot) {
+                    w = *chunk_ptr(x);
+                    stage(x, w);
+                }
+                if (xb < cK) chunk_dots(x, w);
+            }
+        } else {
+            for (int x = tid + PF * NT; x < ctot; x += NT) stage(x, *chunk_ptr(x));   // long logs
+        }
+    }
+    if constexpr (FC && TOKEN) {                        // a . q, summed by the first chunk group
+        float pa = 0.f;
+        if (tid < CPE) pa = dot16<IT>(qpk, apk);
+        pa = group_sum<CPE>(pa);
+        if (tid == 0) s_s = pa;
     }
     if constexpr (HINTED) {
         const int nd = __builtin_amdgcn_readfirstlane(n_dev);
@@ -510,7 +576,19 @@ dl_step_kernel(const StepParams p) {
             if constexpr (SCALAR) {
                 if (tid < n) s_lam[tid] = lamlog[sh * C + tid];
             }
-            for (int x = tid; x < ctot; x += NT) stage(x, *chunk_ptr(x));
+            if constexpr (FC && TOKEN) {
+                for (int xb = 0; xb < ctot; xb += NT) {
+                    const int x = xb + tid;
+                    uint4 w = make_uint4(0, 0, 0, 0);
+                    if (x < ctot) {
+                        w = *chunk_ptr(x);
+                        stage(x, w);
+                    }
+                    if (xb < cK) chunk_dots(x, w);
+                }
+            } else {
+                for (int x = tid; x < ctot; x += NT) stage(x, *chunk_ptr(x));
+            }
         }
     }
     __syncthreads();
@@ -518,15 +596,17 @@ dl_step_kernel(const StepParams p) {
     // ---- 3. replay coefficients: computed here, or (appending units of a
     //         split-replay launch) the ones ReplayPrep left in the scratch,
     //         loaded with the rest of the block's inputs
-    if (fused) {
-        if constexpr (LOG)
-            replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, n, merge, s_lk, s_ll, s_lp, s_lam,
-                                                                     s_qr, s_a, s_cq, s_ck, s_w, s_s);
-        else
-            replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, 0, merge, s_lk, s_ll, s_lp, s_lam,
-                                                                     s_qr, s_a, s_cq, s_ck, s_w, s_s);
+    if constexpr (!FC) {
+        if (fused) {
+            if constexpr (LOG)
+                replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, n, merge, s_lk, s_ll, s_lp, s_lam,
+                                                                         s_qr, s_a, s_cq, s_ck, s_w, s_s);
+            else
+                replay_coefficients<D, NT, KPT, DECAY, DELTA, TOKEN, IT>(tid, 0, merge, s_lk, s_ll, s_lp, s_lam,
+                                                                         s_qr, s_a, s_cq, s_ck, s_w, s_s);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- 4-6. projections, value factor, output, append commit
     if constexpr (TOKEN) {
@@ -535,7 +615,9 @@ dl_step_kernel(const StepParams p) {
         for (int c = 0; c < VEC; ++c) accq[c] = acck[c] = 0.f;
         if constexpr (LOG) {
             for (int i = rg; i < n; i += RG) {             // log entries as extra rows
-                const float cq = s_cq[i], ck = s_ck[i];
+                // staged raw dot products carry their decay weight here
+                const float wi = (FC && SCALAR) ? __expf(s_lp[0] - s_lam[i]) : 1.f;
+                const float cq = s_cq[i] * wi, ck = s_ck[i] * wi;
                 float u[VEC];
                 lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
 #pragma unroll
@@ -672,7 +754,7 @@ dl_step_kernel(const StepParams p) {
         for (int i = 0; i < n; ++i) {
             float u[VEC];
             lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
-            const float w = PERKEY ? 0.f : s_w[i];
+            const float w = PERKEY ? 0.f : (FC ? (SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f) : s_w[i]);
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int r = rg + RG * j;
