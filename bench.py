@@ -65,7 +65,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="2",
-                    help="headline workload: config index 1-5, or gB = GDN fp32 d=128 at batch B")
+                    help="headline workload: config index 1-5, gB = GDN fp32 d=128 at batch B, kB = config 4 at batch B")
     ap.add_argument("--rotate", type=int, default=1, help="independent pools decoded in rotation (headline)")
     ap.add_argument("--value-tile", type=int, default=0,
                     help="value-tile width B_V for the headline pools (0 = library default)")
@@ -667,12 +667,17 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
 
 
 def extra_cfg(tag: str):
-    """Config index 1-5; gB = GDN fp32 d = 128 at batch B; NtpG = config N's
-    per-GPU share under G-way head sharding (H_v / G v-heads, H_k / G q/k heads)."""
+    """Config index 1-5; gB = GDN fp32 d = 128 at batch B; kB = config 4
+    (KDA-style) at batch B; NtpG = config N's per-GPU share under G-way head
+    sharding (H_v / G v-heads, H_k / G q/k heads)."""
     import dataclasses
     from workloads import CONFIGS, headline_gdn
     if tag.startswith("g"):
         return headline_gdn(int(tag[1:]))
+    if tag.startswith("k"):
+        B = int(tag[1:])
+        return dataclasses.replace(CONFIGS[4], index=200 + B, name=f"kda_b{B}_h32_d128", num_slots=B, batch=B,
+                                   seed=CONFIGS[4].seed + B)
     if "tp" in tag:
         idx, G = (int(x) for x in tag.split("tp"))
         base = CONFIGS[idx]

@@ -82,9 +82,11 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *   in_dtype        q, k / a_t and v / b_t inputs: DL_F32 or DL_BF16
  *   value_tile      B_V, columns of the d_k x B_V value tile one GPU work unit
  *                   owns ([DL] GPU-execution section, value tiling); 0 picks the
- *                   library default: 64 for an fp32 state at d = 128, else d,
- *                   except 32 when max_batch * num_v_heads slot-heads would
- *                   give fewer than 256 work units (d >= 64).
+ *                   library default from u = max_batch * num_v_heads: d when
+ *                   u >= 256 or d <= 32; else, at d = 128, 16 when u < 64 and
+ *                   64 when u >= 128 with an fp32 state; else 32.  A default
+ *                   whose live log would exceed the LDS staging budget is
+ *                   halved until it fits or reaches the narrowest built width.
  *                   Built widths: d = 128: 128, 64, 32, 16; d = 64: 64, 32;
  *                   d = 32: 32; d = 16: 16.  Narrower tiles give more work
  *                   units per slot (lower latency at small batch) at the cost

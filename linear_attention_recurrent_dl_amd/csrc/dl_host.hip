@@ -53,8 +53,15 @@ size_t dtype_size(int dt) { return dt == DL_BF16 ? 2 : 4; }
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 int value_tile_of(const dl_pool_desc *d) {
-    return d->value_tile ? d->value_tile
-                         : dl::default_value_tile(d->d_k, d->state_dtype, (long long)d->max_batch * d->num_v_heads);
+    if (d->value_tile) return d->value_tile;
+    int bv = dl::default_value_tile(d->d_k, d->state_dtype, (long long)d->max_batch * d->num_v_heads);
+    // a default whose live log would not fit the LDS staging budget falls back
+    // to the widest narrower tile that does (the value factors shrink with it)
+    while (dl::value_tile_supported(d->d_k, bv / 2) &&
+           dl::log_stage_bytes(d->d_k, bv, d->merge_interval - 1, d->decay, d->update, d->in_dtype) >
+               dl::kMaxLogStageBytes)
+        bv /= 2;
+    return bv;
 }
 
 int validate_desc(const dl_pool_desc *d) {

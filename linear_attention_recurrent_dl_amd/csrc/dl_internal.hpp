@@ -118,16 +118,21 @@ inline size_t log_stage_bytes(int D, int BV, int C, int decay, int update, int i
     return (size_t)C * (D * s_in + BV * s_b + (decay == DECAY_PER_KEY ? D * sizeof(float) : 0));
 }
 
-// Default value-tile width.  Wide tiles (half the row for an fp32 d = 128
-// state, the whole row otherwise) stream best once a batch fills the GPU with
-// blocks; when max_batch * H_v slot-heads would give fewer blocks than the
-// 256 CUs, narrower tiles spread one step over more CUs instead: the widest of
-// 32 or 16 columns that still gives 256 blocks (16 only at d = 128, for 32
-// slot-heads or fewer, where it measured about 2% faster per step).
+// Default value-tile width, by the number of slot-heads a launch may carry
+// (max_batch * H_v).  Once they fill the GPU with blocks, whole-row tiles: one
+// block per slot-head streams its state and replays its log once.  For fp32
+// d = 128 this measured up to 3.5% faster per step than 64-column tiles with
+// per-key decay and up to 3% with scalar decay at B <= 64, and level beyond,
+// although the wider tile holds 3 waves per SIMD instead of 5.  Smaller
+// launches spread one step over more CUs with narrower tiles: 16 columns for
+// 63 slot-heads or fewer at d = 128 (about 2% faster than 32 for 32
+// slot-heads), then 32, and for fp32 d = 128 also 64 below 256 slot-heads, so
+// that a launch keeps at least 256 blocks.
 inline int default_value_tile(int D, int state_dtype, long long units) {
-    const int wide = (D == 128 && state_dtype != BF16) ? 64 : D;
-    if (D >= 64 && units * (D / wide) < 256) return (D == 128 && units * (D / 32) < 256) ? 16 : 32;
-    return wide;
+    if (D < 64) return D;
+    if (D == 128 && units < 64) return 16;
+    if (D == 128 && state_dtype != BF16 && units >= 128 && units < 256) return 64;
+    return units < 256 ? 32 : D;
 }
 // The window kernel stages token inputs in LDS kWindowChunk steps at a time,
 // double buffered: per buffer q, a [K][D], e^{lambda} [K][D] (per-key decay),

@@ -57,10 +57,16 @@ def test_pool_sizes_formula():
         s_b = 4 if cfg.update == "delta" else s_in
         lam_w = {"none": 0, "scalar": 1, "per_key": D}[cfg.decay]
         bv = dl.dl_value_tile(desc)
-        wide = 64 if (D == 128 and cfg.state_dtype == "f32") else D
         units = cfg.batch * Hv
-        narrow = 16 if (D == 128 and units * (D // 32) < 256) else 32
-        assert bv == (narrow if (D >= 64 and units * (D // wide) < 256) else wide), cfg.name
+        if D <= 32 or units >= 256:
+            want = D
+        elif D == 128 and units < 64:
+            want = 16
+        elif D == 128 and cfg.state_dtype == "f32" and units >= 128:
+            want = 64
+        else:
+            want = 32
+        assert bv == want, cfg.name
         assert sz == [P * Hv * D * D * s_st, P * Hk * C * D * s_in, P * Hv * C * D * s_b,
                       P * Hv * C * lam_w * 4, P * Hv * (D // bv) * 4, 0], cfg.name
         # split replay adds one launch's coefficient scratch: 2 L floats per (entry, v-head)
@@ -82,6 +88,20 @@ def test_value_tile_choices(d, bv, ok):
         with pytest.raises(dl.DeltaLogError) as ei:
             dl.dl_value_tile(desc)
         assert ei.value.code == N.DL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d,state,batch,heads,want", [
+    (128, "f32", 1, 32, 16), (128, "f32", 2, 32, 32), (128, "f32", 4, 32, 64), (128, "f32", 7, 32, 64),
+    (128, "f32", 8, 32, 128), (128, "f32", 512, 32, 128), (128, "bf16", 1, 32, 16), (128, "bf16", 4, 32, 32),
+    (128, "bf16", 256, 32, 128), (64, "f32", 1, 32, 32), (64, "f32", 8, 32, 64), (32, "f32", 1, 2, 32),
+    (16, "f32", 1, 2, 16)])
+def test_default_value_tile(d, state, batch, heads, want):
+    """Narrow tiles while a launch's slot-heads would give fewer than 256
+    blocks, whole rows beyond."""
+    desc = dl.make_desc(batch, batch, heads, heads, d, 16, "per_key", "delta", state, "f32")
+    assert dl.dl_value_tile(desc) == want
+    assert dl.dl_value_tile(dl.make_desc(batch, batch, heads, heads, d, 16, "scalar", "delta", state,
+                                         "bf16")) == want
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -244,22 +264,32 @@ def test_host_schedule_serving_pool_workload():
 
 
 def test_merge_sweep_shapes_validate():
-    """Every merge-sweep shape is accepted except KDA at M = 64: its 63 live
-    entries (bf16 keys, fp32 values and per-key snapshots) need 64,512 B of LDS,
-    over the 56 KiB budget, and the pool is refused up front.  GLA's bf16 value
-    factors keep the same log at 56,448 B, inside the budget."""
+    """Every merge-sweep shape is accepted.  At M = 64 the live log of a
+    whole-row tile exceeds the 56 KiB LDS budget, and the default falls back to
+    the widest tile that fits.  KDA's 63 entries (bf16 keys, fp32 values and
+    per-key snapshots) need 80,640 B at 128 columns and 64,512 B at 64, so it
+    gets 32 columns (56,448 B); an explicit wider tile is refused up front."""
     from workloads import SWEEP_OPERATORS, merge_sweep_config
     for op in SWEEP_OPERATORS:
         for M in (1, 2, 4, 8, 16, 32, 64):
             c = merge_sweep_config(op, M)
             desc = dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, M, c.decay, c.update,
                                 c.state_dtype, c.in_dtype)
+            assert dl.dl_pool_sizes(desc)[0] == c.num_slots * c.H_v * c.d * c.d * 4
+            s_in = 2 if c.in_dtype == "bf16" else 4
+            s_b = 4 if c.update == "delta" else s_in
+            snap = c.d * 4 if c.decay == "per_key" else 0
+            want = next(bv for bv in (128, 64, 32, 16)
+                        if (M - 1) * (c.d * s_in + bv * s_b + snap) <= 56 * 1024 or bv == 16)
+            assert dl.dl_value_tile(desc) == want, (op, M)
+            assert want == 128 or M == 64
             if M == 64 and op == "kda":
-                with pytest.raises(dl.DeltaLogError) as ei:
-                    dl.dl_pool_sizes(desc)
-                assert ei.value.code == N.DL_ERR_UNSUPPORTED
-            else:
-                assert dl.dl_pool_sizes(desc)[0] == c.num_slots * c.H_v * c.d * c.d * 4
+                for bv in (128, 64):
+                    wide = dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, M, c.decay, c.update,
+                                        c.state_dtype, c.in_dtype, value_tile=bv)
+                    with pytest.raises(dl.DeltaLogError) as ei:
+                        dl.dl_pool_sizes(wide)
+                    assert ei.value.code == N.DL_ERR_UNSUPPORTED
 
 
 def test_decode_window_rules():
