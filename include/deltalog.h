@@ -22,8 +22,11 @@
  * Conventions shared by every call
  *  - Return value: DL_OK (0) or a negative DL_ERR_* code; dl_last_error()
  *    gives a message (per host thread).  Every argument is validated before
- *    anything is enqueued: a call that fails leaves the pool (host mirror and
- *    device buffers) unchanged.  No C++ exception crosses this ABI.
+ *    anything is enqueued: a call that fails validation leaves the pool (host
+ *    mirror and device buffers) unchanged.  A call split into several launches
+ *    (more slots than dl_launch_slot_limit()) that fails with DL_ERR_HIP on a
+ *    later launch has enqueued the earlier ones but not advanced the host
+ *    mirror; treat the pool as lost then.  No C++ exception crosses this ABI.
  *  - Device work is asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL = the default stream).  Device faults surface as DL_ERR_HIP on a
  *    later call or at the caller's synchronization.
@@ -237,7 +240,11 @@ int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
 /* Materialize the logical state of n slots into their bases and empty their
  * logs ([DL] logical-state equation: S = D(l_bar) S_bar + sum_i
  * D(l_bar - Lambda_i) K_i U_i^T).  Slots with an empty log are left untouched.
- * slot_ids: host int32 [n], distinct, in range. */
+ * slot_ids: host int32 [n], distinct, in range, n <= max_batch.
+ * The slots launched are those the host mirror shows with a live log at the
+ * call; each block then merges what its device counter holds (nothing if
+ * empty).  A merge recorded into a graph therefore covers the slots that were
+ * live at capture, whatever their counters read at replay. */
 int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream);
 
 /* dl_merge over every slot whose log is not empty.  Idempotent. */
