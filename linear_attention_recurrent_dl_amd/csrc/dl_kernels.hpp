@@ -25,7 +25,9 @@
 //      stored
 //   3. replay coefficients per live entry i (TPE threads per entry, DPP sums):
 //      c^q_i = sum_r e^{l'_r - Lam_ir} K_ir q_r, c^k_i likewise with k, and
-//      for a merge the decayed keys e^{l' - Lam_i} * K_i
+//      for a merge the decayed keys e^{l' - Lam_i} * K_i.  With a scalar or
+//      no decay the raw sums K_i . q and K_i . k are instead formed in step 2,
+//      as each key chunk is staged, and weighted e^{l' - Lam_i} where read
 //   4. y_q = S_bar^T q~ + sum_i c^q_i U_i and y_k = S_bar^T k~ + sum_i c^k_i U_i:
 //      per-thread FMAs over its rows, DPP / row-swap sums across the row
 //      groups of a wave, an LDS sum across waves
@@ -208,7 +210,10 @@ struct Tile {
     static constexpr int KPT = sizeof(ST) == 2 ? 4 : 8;
     static constexpr int TPE = D / KPT;                    // threads per log entry
     static constexpr int EPP = NT / TPE;                   // log entries per coefficient pass
-    static constexpr int PF = RPT >= 16 ? 4 : 8;           // log chunks per thread loaded up front
+    // log chunks per thread loaded up front (longer logs stream in a loop);
+    // 4 for bf16 tiles keeps their kernels, with the packed q / a of the
+    // fused replay, within 128 VGPRs (4 waves per SIMD)
+    static constexpr int PF = (RPT >= 16 || sizeof(ST) == 2) ? 4 : 8;
     static_assert(BV % VEC == 0 && D % BV == 0 && NT % CG == 0 && CG <= 64 && TPE <= 64 && NT >= D,
                   "tile geometry");
 };
@@ -319,9 +324,8 @@ dl_step_kernel(const StepParams p) {
     // while the log is staged (one key chunk per thread, DPP sums over the
     // chunk's CPE threads) and weighted e^{l'-Lam_i} where they are read, so
     // there is no separate coefficient pass or barrier.  Per-key decay needs
-    // the snapshot chunk beside each key chunk and keeps the pass; so do bf16
-    // states, whose kernels the packed q / a chunks would push past 128 VGPRs.
-    constexpr bool FC = (MODE == MODE_STEP || MODE == MODE_EAGER) && DECAY != DECAY_PER_KEY && sizeof(ST) == 4;
+    // the snapshot chunk beside each key chunk and keeps the pass.
+    constexpr bool FC = (MODE == MODE_STEP || MODE == MODE_EAGER) && DECAY != DECAY_PER_KEY;
     constexpr int CPE = D / (16 / (int)sizeof(IT));   // 16-byte key chunks per log entry
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
