@@ -203,6 +203,21 @@ def test_longest_log_d128(base_idx, bv):
     _check(cfg, run(cfg, value_tile=bv))
 
 
+def test_longest_per_key_log_default_tile():
+    """KDA-style at d = 128 with L = 64 and 256 slot-heads per launch: the
+    whole-row default tile's 63 live entries (bf16 keys, fp32 values, per-key
+    snapshots) would need 80,640 B of LDS, so the default falls back to 32
+    columns (56,448 B, just inside the budget)."""
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import run
+    cfg = small_variant(CONFIGS[4], batch=64, num_slots=64, steps=140, L=64, d=128, H_v=4, H_k=4,
+                        name="longlog_kda_L64_default_tile")
+    desc = dl.make_desc(cfg.num_slots, cfg.batch, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update,
+                        cfg.state_dtype, cfg.in_dtype)
+    assert dl.dl_value_tile(desc) == 32
+    _check(cfg, run(cfg, track=[0, 21, 63]))
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_eight_v_heads_per_qk_head(split):
     from gpu_harness import run
