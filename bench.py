@@ -644,7 +644,7 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
         # fused replay (every tile unit recomputes its slot-head's coefficients)
         # against split ReplayPrep, by batch and tile width
         for op, mk in (("gdn", lambda B: headline_gdn(B)), ("kda", lambda B: merge_sweep_config("kda", 16, B))):
-            for B, tiles in ((1, (32, 16)), (64, (64, 32)), (128, (64, 32))):
+            for B, tiles in ((1, (32, 16)), (64, (128, 64, 32)), (128, (128, 64, 32))):
                 c = mk(B)
                 R = max(1, int(np.ceil(a.rotate_bytes / pool_bytes(dl, c)))) if B > 1 else 1
                 for bv in tiles:

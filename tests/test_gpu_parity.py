@@ -171,7 +171,7 @@ def test_split_replay_operator_dtype_matrix(combo):
     _check(cfg, run(cfg, value_tile=32, replay_split=True))
 
 
-@pytest.mark.parametrize("d,bv", [(128, 64), (128, 32), (128, 16), (64, 32)])
+@pytest.mark.parametrize("d,bv", [(128, 128), (128, 64), (128, 32), (128, 16), (64, 64), (64, 32)])
 @pytest.mark.parametrize("base_idx", [2, 3, 4, 5])
 def test_split_replay_value_tiles(d, bv, base_idx):
     from gpu_harness import run
