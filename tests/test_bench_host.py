@@ -27,6 +27,10 @@ def test_workload_tags():
     assert bench.extra_cfg("2") == CONFIGS[2]
     g = bench.extra_cfg("g128")
     assert (g.batch, g.num_slots, g.H_v, g.H_k, g.d, g.state_dtype) == (128, 128, 32, 16, 128, "f32")
+    k = bench.extra_cfg("k256")
+    base4 = CONFIGS[4]
+    assert (k.batch, k.num_slots, k.H_v, k.H_k, k.d, k.decay, k.update, k.L) == (
+        256, 256, base4.H_v, base4.H_k, base4.d, base4.decay, base4.update, base4.L)
     share = bench.extra_cfg("5tp8")
     base = CONFIGS[5]
     # one GPU's share under 8-way head sharding: every slot, a slice of the heads
