@@ -310,7 +310,7 @@ dl_step_kernel(const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
-    constexpr int KPT = G::KPT, TPE = G::TPE, EPP = G::EPP, PF = G::PF;
+    constexpr int KPT = G::KPT, PF = G::PF;
     constexpr int NV = D / BV;                    // value tiles per slot-head
     constexpr int KV = 16 / (int)sizeof(IT);      // key-factor elements per 16-byte chunk
     constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte chunk
