@@ -123,3 +123,75 @@ def test_direct_steps_after_a_capture(idx):
     del g
     pool.close()
     assert err.value <= tol and st_e.value <= tol
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_merge_recorded_in_a_graph(idx):
+    """dl_merge recorded into a graph: its launch covers the slots the host saw
+    live at capture, and each block merges whatever its device counter holds
+    at replay (nothing when empty).  Slots outside the recorded set keep their
+    logs; every state and counter follows the oracle."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    base = CONFIGS[idx]
+    cfg = small_variant(base, batch=4, steps=8, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
+                        name=f"graph_merge_{base.name}", random_slots=False, replace_per_step=0,
+                        ragged_fill=False, num_slots=4)
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    P = cfg.num_slots
+    pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, max_batch=P)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    steps = [wl.step_inputs(d) for d in wl.main_steps()]
+    tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
+    err = RelL2()
+
+    def step(s):
+        out = pool.decode_step(s.slot_ids, to_dev(s.q, it), to_dev(s.k, it), to_dev(s.v, it),
+                               to_dev(s.lam, torch.float32), to_dev(s.beta, torch.float32))
+        _, o_ref = E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
+        err.add(out.cpu().numpy(), o_ref)
+
+    def states_match(slots):
+        e = RelL2()
+        e.add(pool.read_base(slots).float().cpu().numpy(), E.states(slots))
+        return e.value
+
+    say(f"[gpu] merge recorded in a graph: {cfg.describe()}")
+    step(steps[0])
+    step(steps[1])                                # every slot holds 2 entries
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pool.merge(np.array([0, 1], dtype=np.int32))
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == 2)     # recorded, not run
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len()[:2] == 0) and np.all(pool.device_log_len()[2:] == 2)
+    assert states_match([0, 1]) <= tol            # their logs are in the bases now
+    g.replay()                                    # empty logs: every block exits at once
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len()[:2] == 0) and states_match([0, 1]) <= tol
+    step(steps[2])                                # host and device agree again: 1, 1, 3, 3
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == np.array([1, 1, 3, 3])[:, None])
+    g.replay()                                    # merges the single entries of slots 0 and 1
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == np.array([0, 0, 3, 3])[:, None])
+    assert states_match([0, 1]) <= tol
+    pool.flush_all()                              # host still counts 1 for slots 0, 1: their blocks exit
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == 0)
+    st_all = states_match(ids)
+    say(f"[gpu]   out rel-L2 {err.value:.3e}, state rel-L2 {st_all:.3e}")
+    del g
+    pool.close()
+    assert err.value <= tol and st_all <= tol
