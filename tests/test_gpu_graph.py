@@ -195,3 +195,62 @@ def test_merge_recorded_in_a_graph(idx):
     del g
     pool.close()
     assert err.value <= tol and st_all <= tol
+
+
+def test_serving_pool_steps_with_assignments_in_a_graph():
+    """The serving pool's step as the benchmark records it: fresh-state
+    assignments, then the decode of random slots, several steps captured in
+    one graph and replayed three times.  Every replay re-assigns the same
+    fresh states and decodes the same tokens; outputs after each replay and
+    the final states follow the oracle."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    cfg = small_variant(CONFIGS[5], batch=4, num_slots=9, steps=6, H_v=4, H_k=2, L=4, replace_per_step=2,
+                        ragged_fill=False, bank_size=8, name="graph_pool_assign")
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    P = cfg.num_slots
+    pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, max_batch=P)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    bank = wl.bank_states()
+    steps = [wl.step_inputs(d) for d in wl.main_steps()]
+    assert all(len(s.replace_ids) == 2 for s in steps)
+    dev = [dict(init=to_dev(bank[s.replace_bank], st), q=to_dev(s.q, it), k=to_dev(s.k, it), v=to_dev(s.v, it),
+                lam=to_dev(s.lam, torch.float32), beta=to_dev(s.beta, torch.float32),
+                out=torch.empty((cfg.batch, cfg.H_v, cfg.d), dtype=torch.float32, device="cuda"))
+           for s in steps]
+    say(f"[gpu] serving-pool steps with assignments in a graph: {cfg.describe()}")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s, d in zip(steps, dev):
+            pool.assign(s.replace_ids, d["init"])
+            pool.decode_step(s.slot_ids, d["q"], d["k"], d["v"], d["lam"], d["beta"], d["out"])
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        err = RelL2()
+        for s, d in zip(steps, dev):
+            E.assign(s.replace_ids, bank[s.replace_bank])
+            _, o_ref = E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
+            err.add(d["out"].cpu().numpy(), o_ref)
+        scratch.mul_(0.5).add_(1.0)
+        torch.cuda.synchronize()
+        say(f"[gpu]   replay {rep}: out rel-L2 {err.value:.3e}")
+        assert err.value <= 2e-2
+    pool.flush_all()
+    st_e = RelL2()
+    st_e.add(pool.read_base(ids).float().cpu().numpy(), E.states())
+    say(f"[gpu]   state rel-L2 {st_e.value:.3e}")
+    del g
+    pool.close()
+    assert st_e.value <= 2e-2
