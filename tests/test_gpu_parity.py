@@ -64,10 +64,13 @@ def test_full_size_sampled(idx):
     _check(cfg, run(cfg, track=TRACK[idx], steps=steps))
 
 
-def test_headline_gdn_batch64_sampled():
+@pytest.mark.parametrize("batch", [64, 256, 512])
+def test_headline_gdn_batch_sampled(batch):
+    """The GDN h32 d128 batch sweep the benchmark times, with its default
+    whole-row tiles, on sampled slots."""
     from gpu_harness import run
-    cfg = headline_gdn(64, steps=64)
-    _check(cfg, run(cfg, track=[0, 63]))
+    cfg = headline_gdn(batch, steps=64 if batch == 64 else 40)
+    _check(cfg, run(cfg, track=[0, batch // 2 + 1, batch - 1]))
 
 
 # ---- eager read-modify-write baseline kernel against the same oracle
