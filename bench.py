@@ -8,10 +8,17 @@ A step is one decode of the workload's batch (for the serving pool: its fresh
 slot assignments, then the decode).  The headline workload is the 32-v-head
 d = 128 GDN decode at batch 1 (fp32 state, merge interval 16).  Inputs are the
 seeded synthetic ones from ``workloads`` and sit in device memory before the
-timed region; W untimed steps precede exactly K timed ones, bracketed by
-device synchronization.  In graph mode the K steps are one captured graph,
-replayed once untimed and then five times, each replay timed on its own; the
-median replay is reported (all five are in the line).  Prints one JSON line.
+timed region; W untimed steps precede K timed ones, bracketed by device
+synchronization.  K is rounded up to whole merge cycles of every rotated pool
+(``steps`` in the line; the requested count is ``steps_requested``), so the
+timed window holds the append/merge mix of the cycle.  In graph mode the K
+steps are one captured graph, replayed once untimed and then five times, each
+replay timed on its own; the median replay is reported.
+
+Output: the last stdout line is one compact JSON object (a few KB): the
+headline, its ``roofline``, ``cpu_baseline``, the eager baseline and one short
+row per other workload.  Every measured row in full goes to stderr as it is
+taken, and to ``--detail FILE`` when given.
 
 ``roofline`` describes the decode kernel: algorithmic bytes per launch (the
 traffic model in ``linear_attention_recurrent_dl_amd.traffic`` summed over the
@@ -88,6 +95,9 @@ def parse(argv=None):
                     help="comma list of workloads whose full logs dl_flush_all materializes ('' = none)")
     ap.add_argument("--windows", default="2:16,2:64,2:256,g128:16,g128:64",
                     help="comma list of workload:W window measurements ('' = none)")
+    ap.add_argument("--detail", default="",
+                    help="also write every measured row (headline, workloads, windows, flushes, host calls) "
+                         "to this JSON file")
     ap.add_argument("--sweep", choices=["merge", "state", "split"], default=None,
                     help="merge-interval, state-size or split-replay sweep instead of the headline line")
     return ap.parse_args(argv)
@@ -709,7 +719,9 @@ def main(argv=None) -> int:
         print(json.dumps(run_sweep(a.sweep, a, torch, dl, native)), flush=True)
         return 0
     cfg = extra_cfg(a.workload)
-    steps, warmup = a.steps, a.warmup
+    # whole merge cycles of every rotated pool, so the timed window holds the
+    # cycle's own mix of append and merge steps
+    steps, warmup = cycle_steps(a.rotate, cfg.L, max(1, a.steps)), a.warmup
     distinct = a.distinct_steps or min(steps + warmup, 4 * cfg.L)
     print(f"[bench] headline {cfg.describe()} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
 
@@ -783,55 +795,113 @@ def main(argv=None) -> int:
         cpu = cpu_baseline(cfg, a.cpu_seconds)
         print(f"[bench] cpu {json.dumps(cpu)}", file=sys.stderr, flush=True)
 
-    traffic_val = None
-    prof = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_r{a.rotate}.json")
+    traffic_val, traffic_src = None, None
+    prof = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}_rot{a.rotate}.json")
     if os.path.exists(prof):
         try:
             with open(prof) as f:
                 pj = json.load(f)
             if pj.get("kernel_source_hash") == kernel_source_hash():
                 traffic_val = pj.get("hbm_bytes_per_launch")
+                traffic_src = os.path.relpath(prof, ROOT)
         except Exception:
             traffic_val = None
 
+    detail = {"headline": head, "eager_baseline": eager_head, "workloads": extras, "windows": windows,
+              "flush": flushes, "host_call": host_cost, "stream_reference": stream_ref, "cpu_baseline": cpu,
+              "kernel_source_hash": kernel_source_hash()}
+    print(f"[bench] detail {json.dumps(detail)}", file=sys.stderr, flush=True)
+    if a.detail:
+        os.makedirs(os.path.dirname(os.path.abspath(a.detail)), exist_ok=True)
+        with open(a.detail, "w") as f:
+            json.dump(detail, f, indent=1)
+    line = make_line(cfg, a.rotate, steps, warmup, a.steps, head, eager_head, extras, windows, flushes, cpu,
+                     traffic_val, traffic_src, kernel_source_hash())
+    print(json.dumps(line, separators=(",", ":")), flush=True)
+    return 0
+
+
+def line_dtype(cfg) -> str:
+    """Arithmetic type of the path: the kernels compute in fp32; 16-bit state
+    or inputs are widened on load (named after it)."""
+    if cfg.state_dtype == "f32" and cfg.in_dtype == "f32":
+        return "f32"
+    return f"f32 ({cfg.state_dtype} state, {cfg.in_dtype} inputs)"
+
+
+def _r(x, nd):
+    return None if x is None else round(float(x), nd)
+
+
+def compact_rows(extras) -> list:
+    """One short row per extra workload: DeltaLog and its eager baseline side by
+    side (us per decode launch, algorithmic GB/s, fraction of 8 TB/s)."""
+    rows, index = [], {}
+    for s in extras:
+        key = s["workload"]
+        if key not in index:
+            index[key] = {"w": key, "B": s["batch"], "st": s["state"], "R": s.get("rotated_pools")}
+            rows.append(index[key])
+        row = index[key]
+        if s["kernel"] == "eager":
+            row["eager_us"] = _r(s["decode_launch_us"], 2)
+            row["eager_GBps"] = _r(s["decode_GBps"], 0)
+        else:
+            row.update({"tile": s["value_tile"], "us": _r(s["decode_launch_us"], 2), "GBps": _r(s["decode_GBps"], 0),
+                        "frac": _r(s["decode_frac_of_8TBps"], 3), "Mhs": _r(s["head_steps_per_s"] / 1e6, 2)})
+    for row in rows:
+        if row.get("us") and row.get("eager_us"):
+            row["x_eager"] = _r(row["eager_us"] / row["us"], 3)
+    return rows
+
+
+def make_line(cfg, rotate, steps, warmup, steps_requested, head, eager_head, extras, windows, flushes, cpu,
+              traffic_val, traffic_src, khash) -> dict:
+    """The one JSON line on stdout: headline, roofline of the decode kernel,
+    CPU baseline, eager baseline and one short row per other workload.  Kept
+    to a few KB; the full detail goes to stderr (and --detail)."""
     line = {
         "metric": "decode head-steps/s + achieved HBM GB/s vs 8 TB/s peak, GDN h=32 d=128",
         "value": head["head_steps_per_s"],
         "unit": "head-steps/s",
         "n_gpus": 1,
         "steps": steps,
+        "steps_requested": steps_requested,
         "warmup": warmup,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "rotated_pools": a.rotate, "global_batch": cfg.batch, "v_heads": cfg.H_v,
-                   "qk_heads": cfg.H_k, "d_k": cfg.d, "d_v": cfg.d, "state": cfg.state_dtype,
-                   "merge_interval": cfg.L, "value_tile": head["value_tile"], "parallelism": "single-gpu"},
-        "tokens_per_s": head["tokens_per_s"],
-        "roofline": {"bound": "hbm", "achieved": head["decode_GBps"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": head["decode_GBps"] / PEAK_HBM_GBS,
-                     "traffic": traffic_val,
-                     "traffic_source": os.path.relpath(prof, ROOT) if traffic_val is not None else None,
+        "dtype": line_dtype(cfg),
+        "data": "synthetic (seeded)",
+        "config": {"workload": cfg.name, "global_batch": cfg.batch, "v_heads": cfg.H_v, "qk_heads": cfg.H_k,
+                   "d_k": cfg.d, "d_v": cfg.d, "state": cfg.state_dtype, "inputs": cfg.in_dtype,
+                   "merge_interval": cfg.L, "value_tile": head["value_tile"], "rotated_pools": rotate,
+                   "parallelism": "single-gpu"},
+        "tokens_per_s": _r(head["tokens_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": _r(head["decode_GBps"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": _r(head["decode_GBps"] / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_val, "traffic_source": traffic_src,
                      "kernel": "dl_step_kernel (decode, append/merge)",
-                     "bytes_per_launch": head["decode_bytes_per_launch"],
-                     "launch_us": head["decode_launch_us"],
-                     "launch_source": head["decode_launch_source"],
-                     "launch_us_event_pair": head["launch_mode"]["decode_event_pair_us_avg"]},
-        "launch_mode": head["launch_mode"],
-        "cpu_baseline": cpu,
-        "eager_baseline": eager_head,
-        "workloads": extras,
-        "windows": windows,
-        "flush": flushes,
-        "host_call": host_cost,
-        "stream_reference": stream_ref,
-        "kernel_source_hash": kernel_source_hash(),
+                     "bytes_per_launch": _r(head["decode_bytes_per_launch"], 1),
+                     "launch_us": _r(head["decode_launch_us"], 3),
+                     "launch_source": head["decode_launch_source"]},
+        "cpu_baseline": None if cpu is None else {
+            "value": _r(cpu["value"], 1), "unit": cpu["unit"], "cores": cpu["cores"], "kind": cpu["kind"],
+            "sample": cpu["sample"]},
+        "eager_baseline": None if eager_head is None else {
+            "us_per_step": _r(eager_head["ms_per_step"] * 1e3, 3),
+            "head_steps_per_s": _r(eager_head["head_steps_per_s"], 1),
+            "GBps": _r(eager_head["decode_GBps"], 1),
+            "deltalog_speedup": _r(eager_head["ms_per_step"] / head["ms_per_step"], 3)},
+        "workloads": compact_rows(extras),
+        "windows": [{"w": w["workload"], "W": w["W"], "us_step": _r(w["us_per_step"], 3),
+                     "x_decode": _r(w.get("speedup_per_step_vs_decode"), 2)} for w in windows],
+        "flush": [{"w": f["workload"], "us": _r(f["launch_us"], 1), "frac": _r(f["frac_of_8TBps"], 3)}
+                  for f in flushes],
+        "kernel_source_hash": khash,
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 if __name__ == "__main__":

@@ -25,8 +25,10 @@
  *    anything is enqueued: a call that fails validation leaves the pool (host
  *    mirror and device buffers) unchanged.  A call split into several launches
  *    (more slots than dl_launch_slot_limit()) that fails with DL_ERR_HIP on a
- *    later launch has enqueued the earlier ones but not advanced the host
- *    mirror; treat the pool as lost then.  No C++ exception crosses this ABI.
+ *    later launch has enqueued the earlier launches and advanced the host
+ *    mirror for their slots only: the slots of the failed launch and of those
+ *    after it are unchanged on host and device.  No C++ exception crosses
+ *    this ABI.
  *  - Device work is asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL = the default stream).  Device faults surface as DL_ERR_HIP on a
  *    later call or at the caller's synchronization.
@@ -198,7 +200,8 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids,
  * and advances the host's live lengths as if they had run.  The kernels take
  * each slot's phase (append or merge, entry index) from the device counters,
  * so a captured step stays correct when replayed at any point of the cycle;
- * dl_get_log_len then reflects the calls made, not the replays.  A direct
+ * dl_get_log_len then reflects the calls made, not the replays, and the pool
+ * counts its host mirror as stale from then on (see dl_flush_all).  A direct
  * call also passes the host's live lengths to the kernels, which use them to
  * start loading the log early and fall back to the device counters when they
  * differ (as after a capture); captured launches pass none. */
@@ -241,13 +244,19 @@ int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
  * logs ([DL] logical-state equation: S = D(l_bar) S_bar + sum_i
  * D(l_bar - Lambda_i) K_i U_i^T).  Slots with an empty log are left untouched.
  * slot_ids: host int32 [n], distinct, in range, n <= max_batch.
- * The slots launched are those the host mirror shows with a live log at the
- * call; each block then merges what its device counter holds (nothing if
- * empty).  A merge recorded into a graph therefore covers the slots that were
- * live at capture, whatever their counters read at replay. */
+ * Every listed slot is launched, and each of its blocks merges what its
+ * device counter holds when it runs (nothing if empty), so the result does
+ * not depend on the host mirror: a merge recorded into a graph merges, at
+ * each replay, the listed slots' logs as they are then.  The host mirror of
+ * the listed slots becomes 0. */
 int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream);
 
-/* dl_merge over every slot whose log is not empty.  Idempotent. */
+/* dl_merge over every slot whose log is not empty; afterwards every log is
+ * empty and every base is its slot's logical state.  Idempotent.  The host
+ * mirror selects the slots while it follows the device; once any call on the
+ * pool has been recorded into a graph (including this one), replays may have
+ * moved the device counters without it, and every slot of the pool is
+ * launched instead (blocks of empty slots exit at once). */
 int dl_flush_all(dl_pool *pool, void *stream);
 
 /* Copy the bases of n slots out in the natural layout.

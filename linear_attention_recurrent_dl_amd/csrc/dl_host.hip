@@ -21,6 +21,7 @@
 
 #include "deltalog.h"
 #include "dl_internal.hpp"
+#include "dl_mirror.hpp"
 
 namespace dl {
 template <int D, int BV>
@@ -178,6 +179,8 @@ struct dl_pool {
     int nv;                         // value tiles per slot-head
     bool dry;                       // host-only pool: validate + mirror, no device work
     std::vector<int32_t> n;         // host mirror of live-log length per slot
+    bool stale;                     // a call was recorded into a graph: replays move the
+                                    // device counters without the mirror
     std::vector<uint32_t> seen;     // duplicate detection (generation stamps)
     uint32_t gen;
 };
@@ -207,6 +210,21 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(DL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Whether work enqueued on `stream` now is recorded into a graph instead of
+// run.  A call recorded into a graph marks the pool's mirror stale: its
+// replays move the device counters and the mirror does not follow them.
+bool capturing(dl_pool *pool, void *stream) {
+    if (pool->dry) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    bool cap = true;                            // unknown: assume recorded
+    if (hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess)
+        cap = cs != hipStreamCaptureStatusNone;
+    else
+        (void)hipGetLastError();
+    if (cap) pool->stale = true;
+    return cap;
+}
+
 // Natural-layout states in or out of the pool's tile-major base, split into
 // launches of at most kMaxLaunchSlots slots.  ext: [n, H_v, d_k, d_v].
 int copy_states(dl_pool *pool, int32_t n, const int32_t *ids, void *ext, bool to_pool, void *stream) {
@@ -223,15 +241,17 @@ int copy_states(dl_pool *pool, int32_t n, const int32_t *ids, void *ext, bool to
     p.D = d.d_k;
     p.H_v = d.num_v_heads;
     p.NV = pool->nv;
-    for (int32_t lo = 0; lo < n; lo += dl::kMaxLaunchSlots) {
-        const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, n - lo);
+    auto launch = [&](int32_t lo, int32_t cnt) -> int {
+        if (pool->dry) return hipSuccess;
         p.ext = ext ? static_cast<char *>(ext) + (size_t)lo * d.num_v_heads * head_bytes : nullptr;
         p.nunits = cnt * d.num_v_heads;
         memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
-        const int e = dl::launch_copy(p, (hipStream_t)stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+        return dl::launch_copy(p, (hipStream_t)stream);
+    };
+    auto commit = [&](int32_t lo, int32_t cnt) {
+        if (to_pool) dl::mirror_clear(pool->n.data(), ids + lo, cnt);
+    };
+    return dl::launch_chunks(n, dl::kMaxLaunchSlots, launch, commit);
 }
 
 // Shared by dl_decode_step and dl_eager_step.
@@ -261,12 +281,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
         // A launch recorded into a graph may be replayed at any phase of the
         // append-merge cycle, so it carries no live lengths from the host.
-        bool capturing = true;
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess)
-            capturing = cs != hipStreamCaptureStatusNone;
-        else
-            (void)hipGetLastError();            // unknown: take the counter, always correct
+        const bool cap = capturing(pool, stream);
         dl::StepParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -279,8 +294,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         p.H_k = d.num_k_heads;
         p.C = C;
         p.NV = pool->nv;
-        for (int32_t lo = 0; lo < B; lo += dl::kMaxLaunchSlots) {
-            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, B - lo);
+        auto launch = [&](int32_t lo, int32_t cnt) -> int {
             p.q = static_cast<const char *>(q) + (size_t)lo * Hk * D * s_in;
             p.k = static_cast<const char *>(a_or_k) + (size_t)lo * Hk * D * s_in;
             p.v = static_cast<const char *>(b_or_v) + (size_t)lo * Hv * D * s_in;
@@ -290,7 +304,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
             if (mode == dl::MODE_STEP) {         // the host's live lengths ride in the slot words
                 for (int32_t j = 0; j < cnt; ++j)
-                    p.slots[j] |= (capturing ? dl::kNoHint : (uint32_t)pool->n[ids[lo + j]]) << dl::kSlotBits;
+                    p.slots[j] |= (cap ? dl::kNoHint : (uint32_t)pool->n[ids[lo + j]]) << dl::kSlotBits;
             }
             if (split) {
                 // ReplayPrep, one block per (entry, v-head), into the coefficient scratch
@@ -303,14 +317,46 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             const int e = dl::launch_step(d.d_k, pool->bv, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p,
                                           shmem, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail((hipError_t)e, "decode kernel launch");
-        }
+            return DL_OK;
+        };
+        auto commit = [&](int32_t lo, int32_t cnt) { dl::mirror_decode(pool->n.data(), ids + lo, cnt, C); };
+        rc = dl::launch_chunks(B, dl::kMaxLaunchSlots, launch, commit);
+        return rc ? rc : ok();
     }
-    const int32_t C = d.merge_interval - 1;
-    for (int32_t j = 0; j < B; ++j) {
-        int32_t &n = pool->n[ids[j]];
-        n = (n == C) ? 0 : n + 1;
-    }
+    dl::mirror_decode(pool->n.data(), ids, B, d.merge_interval - 1);
     return ok();
+}
+
+// Standalone merges of the given (validated, distinct) slots.  Every slot is
+// launched: a block whose device counter reads 0 exits at once, so the set
+// does not depend on the host mirror, which a graph replay leaves behind.
+int merge_slots(dl_pool *pool, int32_t n, const int32_t *ids, void *stream) {
+    const dl_pool_desc &d = pool->desc;
+    const int C = d.merge_interval - 1;
+    if (!pool->dry) (void)capturing(pool, stream);
+    dl::StepParams p;
+    memset(&p, 0, sizeof p);
+    p.base = pool->buf.base;
+    p.klog = pool->buf.klog;
+    p.ulog = pool->buf.ulog;
+    p.lamlog = pool->buf.lamlog;
+    p.nlog = pool->buf.nlog;
+    p.H_v = d.num_v_heads;
+    p.H_k = d.num_k_heads;
+    p.C = C;
+    p.NV = pool->nv;
+    const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+    auto launch = [&](int32_t lo, int32_t cnt) -> int {
+        if (pool->dry || C == 0) return DL_OK;     // no log to merge in an eager pool
+        p.nunits = cnt * d.num_v_heads * pool->nv;
+        memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+        const int e = dl::launch_step(d.d_k, pool->bv, dl::MODE_MERGE, d.decay, d.update, d.state_dtype,
+                                      d.in_dtype, p, shmem, (hipStream_t)stream);
+        return e != hipSuccess ? hip_fail((hipError_t)e, "merge kernel launch") : DL_OK;
+    };
+    auto commit = [&](int32_t lo, int32_t cnt) { dl::mirror_clear(pool->n.data(), ids + lo, cnt); };
+    const int rc = dl::launch_chunks(n, dl::kMaxLaunchSlots, launch, commit);
+    return rc ? rc : ok();
 }
 
 }  // namespace
@@ -351,6 +397,7 @@ int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_
     p->n.assign(desc->num_slots, 0);
     p->seen.assign(desc->num_slots, 0u);
     p->gen = 0;
+    p->stale = false;
     if (!p->dry) {
         const size_t cnt = sz[DL_BUF_NLOG] / 4;
         const int blocks = (int)std::min<size_t>((cnt + 255) / 256, 4096);
@@ -377,11 +424,10 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids, const void
     if (rc) return rc;
     if (init_base && ((uintptr_t)init_base & 15)) return fail(DL_ERR_INVALID_ARG, "init_base is not 16-byte aligned");
     if (n == 0) return ok();
-    if (!pool->dry) {
-        const int e = copy_states(pool, n, slot_ids, const_cast<void *>(init_base), true, stream);
-        if (e != hipSuccess) return hip_fail((hipError_t)e, "assign kernel launch");
-    }
-    for (int32_t j = 0; j < n; ++j) pool->n[slot_ids[j]] = 0;
+    (void)capturing(pool, stream);
+    // the mirror is cleared launch by launch (a host-only pool launches nothing)
+    const int e = copy_states(pool, n, slot_ids, const_cast<void *>(init_base), true, stream);
+    if (e != hipSuccess) return hip_fail((hipError_t)e, "assign kernel launch");
     return ok();
 }
 
@@ -430,6 +476,7 @@ int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t 
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
         const size_t shmem = dl::window_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+        (void)capturing(pool, stream);
         dl::WindowParams p;
         memset(&p, 0, sizeof p);
         p.base = pool->buf.base;
@@ -443,8 +490,7 @@ int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t 
         p.NV = pool->nv;
         p.W = W;
         p.B = B;
-        for (int32_t lo = 0; lo < B; lo += dl::kMaxLaunchSlots) {
-            const int32_t cnt = std::min<int32_t>(dl::kMaxLaunchSlots, B - lo);
+        auto launch = [&](int32_t lo, int32_t cnt) -> int {
             p.q = static_cast<const char *>(q) + (size_t)lo * Hk * D * s_in;
             p.k = static_cast<const char *>(a_or_k) + (size_t)lo * Hk * D * s_in;
             p.v = static_cast<const char *>(b_or_v) + (size_t)lo * Hv * D * s_in;
@@ -455,10 +501,14 @@ int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t 
             p.nunits = cnt * d.num_v_heads * pool->nv;
             const int e = dl::launch_window(d.d_k, pool->bv, d.decay, d.update, d.state_dtype, d.in_dtype, p, shmem,
                                             (hipStream_t)stream);
-            if (e != hipSuccess) return hip_fail((hipError_t)e, "window kernel launch");
-        }
+            return e != hipSuccess ? hip_fail((hipError_t)e, "window kernel launch") : DL_OK;
+        };
+        // the window leaves every log it covers empty
+        auto commit = [&](int32_t lo, int32_t cnt) { dl::mirror_clear(pool->n.data(), slot_ids + lo, cnt); };
+        rc = dl::launch_chunks(B, dl::kMaxLaunchSlots, launch, commit);
+        return rc ? rc : ok();
     }
-    for (int32_t j = 0; j < B; ++j) pool->n[slot_ids[j]] = 0;   // the window leaves every log empty
+    dl::mirror_clear(pool->n.data(), slot_ids, B);
     return ok();
 }
 
@@ -466,50 +516,22 @@ int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream) {
     if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
     int rc = check_slots(pool, n, slot_ids);
     if (rc) return rc;
-    const dl_pool_desc &d = pool->desc;
-    // only slots with a non-empty log have anything to materialize
-    std::vector<int32_t> live;
-    live.reserve(n);
-    for (int32_t j = 0; j < n; ++j)
-        if (pool->n[slot_ids[j]] > 0) live.push_back(slot_ids[j]);
-    if (!pool->dry && !live.empty()) {
-        const int C = d.merge_interval - 1;
-        dl::StepParams p;
-        memset(&p, 0, sizeof p);
-        p.base = pool->buf.base;
-        p.klog = pool->buf.klog;
-        p.ulog = pool->buf.ulog;
-        p.lamlog = pool->buf.lamlog;
-        p.nlog = pool->buf.nlog;
-        p.H_v = d.num_v_heads;
-        p.H_k = d.num_k_heads;
-        p.C = C;
-        p.NV = pool->nv;
-        const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
-        for (size_t lo = 0; lo < live.size(); lo += dl::kMaxLaunchSlots) {
-            const int32_t cnt = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, live.size() - lo);
-            p.nunits = cnt * d.num_v_heads * pool->nv;
-            memcpy(p.slots, live.data() + lo, cnt * sizeof(int32_t));
-            const int e = dl::launch_step(d.d_k, pool->bv, dl::MODE_MERGE, d.decay, d.update, d.state_dtype,
-                                          d.in_dtype, p, shmem, (hipStream_t)stream);
-            if (e != hipSuccess) return hip_fail((hipError_t)e, "merge kernel launch");
-        }
-    }
-    for (int32_t s : live) pool->n[s] = 0;
-    return ok();
+    if (n == 0) return ok();
+    return merge_slots(pool, n, slot_ids, stream);
 }
 
 int dl_flush_all(dl_pool *pool, void *stream) {
     if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    // The mirror picks the slots with a live log while it follows the device;
+    // once a call has been recorded into a graph (or this one would be), the
+    // device counters may hold entries the mirror does not show, so every
+    // slot is launched and each block merges what its counter holds.
+    const bool all = capturing(pool, stream) || pool->stale;
     std::vector<int32_t> live;
     for (int32_t s = 0; s < pool->desc.num_slots; ++s)
-        if (pool->n[s] > 0) live.push_back(s);
-    for (size_t lo = 0; lo < live.size(); lo += pool->desc.max_batch) {
-        const int32_t cnt = (int32_t)std::min<size_t>(pool->desc.max_batch, live.size() - lo);
-        int rc = dl_merge(pool, cnt, live.data() + lo, stream);
-        if (rc) return rc;
-    }
-    return ok();
+        if (all || pool->n[s] > 0) live.push_back(s);
+    if (live.empty()) return ok();
+    return merge_slots(pool, (int32_t)live.size(), live.data(), stream);
 }
 
 int dl_get_log_len(const dl_pool *pool, int32_t *n_out) {

@@ -46,3 +46,55 @@ def test_more_than_one_gpu_is_refused():
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["requested_gpus"] == 2 and "one GPU" in line["error"]
     assert "--gpus 1" in r.stderr
+
+
+def _synthetic_rows():
+    """Measured rows shaped as bench.summarize / time_window / time_flush give them."""
+    from workloads import CONFIGS
+    head = {"workload": "gdn_b1_h32_d128", "kernel": "deltalog", "batch": 1, "state": "f32", "value_tile": 16,
+            "head_steps_per_s": 8.75e6, "tokens_per_s": 2.73e5, "ms_per_step": 3.66e-3, "decode_GBps": 680.1,
+            "decode_frac_of_8TBps": 0.085, "decode_bytes_per_launch": 2.49e6, "decode_launch_us": 3.66,
+            "decode_launch_source": "graph replay, back-to-back launches"}
+    eager = dict(head, kernel="eager", ms_per_step=3.0e-3, head_steps_per_s=1.07e7, decode_GBps=1400.0)
+    extras = []
+    for tag in ("1", "3", "4", "5", "5tp8", "g64", "g128", "g256", "g512"):
+        c = bench.extra_cfg(tag)
+        for k, us in (("deltalog", 50.123456), ("eager", 90.987654)):
+            extras.append({"workload": c.name, "kernel": k, "batch": c.batch, "state": c.state_dtype,
+                           "value_tile": 128, "decode_launch_us": us, "decode_GBps": 5712.345678,
+                           "decode_frac_of_8TBps": 0.714043, "head_steps_per_s": 1.234567e8, "rotated_pools": 4,
+                           "long_field_that_stays_in_the_detail": "x" * 500})
+    windows = [{"workload": "gdn_b1_h32_d128", "W": w, "us_per_step": 0.71, "speedup_per_step_vs_decode": 5.1}
+               for w in (16, 64, 256)]
+    flushes = [{"workload": "gdn_b256_h32_d128", "launch_us": 205.9, "frac_of_8TBps": 0.71}]
+    cpu = {"value": 4.0e4, "unit": "head-steps/s", "cores": 1, "kind": "oracle",
+           "sample": "64 steps of gdn_b1_h32_d128 (all 32 slot-heads each), fp64 NumPy eager recurrence, 12.0 s wall",
+           "cpu_model": "some CPU", "blas_threads": 1}
+    return CONFIGS[2], head, eager, extras, windows, flushes, cpu
+
+
+def test_stdout_line_is_compact_and_parses():
+    cfg, head, eager, extras, windows, flushes, cpu = _synthetic_rows()
+    steps = bench.cycle_steps(1, cfg.L, 20)
+    line = bench.make_line(cfg, 1, steps, 5, 20, head, eager, extras, windows, flushes, cpu, 2629074.0,
+                           "profiles/traffic_gdn_b1_h32_d128_rot1.json", "0123456789abcdef")
+    text = json.dumps(line, separators=(",", ":"))
+    assert len(text.encode()) <= 4096, len(text)
+    back = json.loads(text)
+    assert back["steps"] == 32 and back["steps_requested"] == 20 and back["warmup"] == 5
+    assert back["dtype"] == "f32" and back["config"]["workload"] == cfg.name
+    for k in ("metric", "value", "unit", "ms_per_step", "roofline", "cpu_baseline", "eager_baseline", "workloads"):
+        assert k in back
+    rf = back["roofline"]
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert set(back["cpu_baseline"]) == {"value", "unit", "cores", "kind", "sample"}
+    names = [w["w"] for w in back["workloads"]]
+    assert len(names) == 9 and len(set(names)) == 9
+    assert all("x_eager" in w and "frac" in w for w in back["workloads"])
+
+
+def test_line_dtype_names_the_storage_of_16_bit_workloads():
+    from workloads import CONFIGS
+    assert bench.line_dtype(CONFIGS[2]) == "f32"
+    assert bench.line_dtype(CONFIGS[5]).startswith("f32") and "bf16" in bench.line_dtype(CONFIGS[5])

@@ -71,12 +71,14 @@ def test_graph_replay_matches_oracle(idx, value_tile, split):
     pool.close()
 
 
-@pytest.mark.parametrize("idx", [2, 4, 5])
-def test_direct_steps_after_a_capture(idx):
+@pytest.mark.parametrize("idx,steps", [(2, 14), (4, 14), (5, 14), (2, 12), (5, 12)])
+def test_direct_steps_after_a_capture(idx, steps):
     """Capturing steps advances the host's live lengths but not the device's.
     Direct steps afterwards carry host values that differ from the device
     counters, so every block restages its log from the counter; outputs,
-    states and device counters must follow the direct steps alone."""
+    states and device counters must follow the direct steps alone.  With 12
+    steps (3 captured, 9 direct, L = 4) the host mirror ends at 0 while every
+    device log holds 1 entry: dl_flush_all must still merge it."""
     import torch
 
     import linear_attention_recurrent_dl_amd as dl
@@ -84,7 +86,7 @@ def test_direct_steps_after_a_capture(idx):
     from oracle import EagerPool, RelL2, schedule
 
     base = CONFIGS[idx]
-    cfg = small_variant(base, batch=3, steps=14, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
+    cfg = small_variant(base, batch=3, steps=steps, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
                         name=f"capture_then_direct_{base.name}", random_slots=False, replace_per_step=0,
                         ragged_fill=False, num_slots=3)
     wl = Workload(cfg)
@@ -115,7 +117,10 @@ def test_direct_steps_after_a_capture(idx):
         err.add(out.cpu().numpy(), o_ref)
     torch.cuda.synchronize()
     assert np.all(pool.device_log_len() == cnt.n[:, None])
+    assert np.all(pool.log_len() == (3 + steps - 3) % cfg.L)     # the mirror counts the captured calls too
     pool.flush_all()
+    torch.cuda.synchronize()
+    assert np.all(pool.device_log_len() == 0)
     st_e = RelL2()
     st_e.add(pool.read_base(ids).float().cpu().numpy(), E.states())
     tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
@@ -127,10 +132,10 @@ def test_direct_steps_after_a_capture(idx):
 
 @pytest.mark.parametrize("idx", [2, 5])
 def test_merge_recorded_in_a_graph(idx):
-    """dl_merge recorded into a graph: its launch covers the slots the host saw
-    live at capture, and each block merges whatever its device counter holds
-    at replay (nothing when empty).  Slots outside the recorded set keep their
-    logs; every state and counter follows the oracle."""
+    """dl_merge recorded into a graph: its launch covers the listed slots, and
+    each block merges whatever its device counter holds at replay (nothing
+    when empty).  Slots outside the recorded set keep their logs; every state
+    and counter follows the oracle."""
     import torch
 
     import linear_attention_recurrent_dl_amd as dl
@@ -187,7 +192,7 @@ def test_merge_recorded_in_a_graph(idx):
     torch.cuda.synchronize()
     assert np.all(pool.device_log_len() == np.array([0, 0, 3, 3])[:, None])
     assert states_match([0, 1]) <= tol
-    pool.flush_all()                              # host still counts 1 for slots 0, 1: their blocks exit
+    pool.flush_all()                              # mirror stale since the capture: every slot is launched
     torch.cuda.synchronize()
     assert np.all(pool.device_log_len() == 0)
     st_all = states_match(ids)
@@ -195,6 +200,65 @@ def test_merge_recorded_in_a_graph(idx):
     del g
     pool.close()
     assert err.value <= tol and st_all <= tol
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_flush_after_replays_the_mirror_missed(idx):
+    """Two direct steps, then two steps captured and replayed twice (L = 4):
+    the host mirror reads 0 entries, every device log holds 2.  dl_flush_all
+    (and dl_merge) must materialize those logs: the bases then equal the
+    oracle's states after all six decodes, and every counter reads 0."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    base = CONFIGS[idx]
+    cfg = small_variant(base, batch=3, steps=4, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
+                        name=f"replays_then_flush_{base.name}", random_slots=False, replace_per_step=0,
+                        ragged_fill=False, num_slots=3)
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    P = cfg.num_slots
+    tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
+    for how in ("flush_all", "merge"):
+        say(f"[gpu] replays the mirror missed, then {how}: {cfg.describe()}")
+        pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                               cfg.in_dtype, max_batch=cfg.batch)
+        ids = np.arange(P, dtype=np.int32)
+        pool.assign(ids, to_dev(wl.init_base(ids), st))
+        E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+        steps = [wl.step_inputs(d) for d in wl.main_steps()]
+        dev = [dict(q=to_dev(s.q, it), k=to_dev(s.k, it), v=to_dev(s.v, it), lam=to_dev(s.lam, torch.float32),
+                    beta=to_dev(s.beta, torch.float32)) for s in steps]
+        for s, d in zip(steps[:2], dev[:2]):
+            pool.decode_step(s.slot_ids, d["q"], d["k"], d["v"], d["lam"], d["beta"])
+            E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s, d in zip(steps[2:], dev[2:]):
+                pool.decode_step(s.slot_ids, d["q"], d["k"], d["v"], d["lam"], d["beta"])
+        for _ in range(2):
+            g.replay()
+            torch.cuda.synchronize()
+            for s in steps[2:]:
+                E.step(s.slot_ids, s.q, s.k, s.v, s.lam, s.beta)
+        assert np.all(pool.log_len() == 0) and np.all(pool.device_log_len() == 2)
+        if how == "flush_all":
+            pool.flush_all()
+        else:
+            pool.merge(ids)
+        torch.cuda.synchronize()
+        n_dev = pool.device_log_len()
+        e = RelL2()
+        e.add(pool.read_base(ids).float().cpu().numpy(), E.states())
+        say(f"[gpu]   state rel-L2 {e.value:.3e}, device n {sorted(set(n_dev.ravel().tolist()))}")
+        del g
+        pool.close()
+        assert np.all(n_dev == 0)
+        assert e.value <= tol
 
 
 def test_serving_pool_steps_with_assignments_in_a_graph():
