@@ -71,8 +71,8 @@ def test_graph_replay_matches_oracle(idx, value_tile, split):
     pool.close()
 
 
-@pytest.mark.parametrize("idx,steps", [(2, 14), (4, 14), (5, 14), (2, 12), (5, 12)])
-def test_direct_steps_after_a_capture(idx, steps):
+@pytest.mark.parametrize("idx,nsteps", [(2, 14), (4, 14), (5, 14), (2, 12), (5, 12)])
+def test_direct_steps_after_a_capture(idx, nsteps):
     """Capturing steps advances the host's live lengths but not the device's.
     Direct steps afterwards carry host values that differ from the device
     counters, so every block restages its log from the counter; outputs,
@@ -86,7 +86,7 @@ def test_direct_steps_after_a_capture(idx, steps):
     from oracle import EagerPool, RelL2, schedule
 
     base = CONFIGS[idx]
-    cfg = small_variant(base, batch=3, steps=steps, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
+    cfg = small_variant(base, batch=3, steps=nsteps, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=4,
                         name=f"capture_then_direct_{base.name}", random_slots=False, replace_per_step=0,
                         ragged_fill=False, num_slots=3)
     wl = Workload(cfg)
@@ -117,7 +117,7 @@ def test_direct_steps_after_a_capture(idx, steps):
         err.add(out.cpu().numpy(), o_ref)
     torch.cuda.synchronize()
     assert np.all(pool.device_log_len() == cnt.n[:, None])
-    assert np.all(pool.log_len() == (3 + steps - 3) % cfg.L)     # the mirror counts the captured calls too
+    assert np.all(pool.log_len() == nsteps % cfg.L)     # the mirror counts the captured calls too
     pool.flush_all()
     torch.cuda.synchronize()
     assert np.all(pool.device_log_len() == 0)
