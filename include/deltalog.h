@@ -142,7 +142,9 @@ typedef struct {
  *                                                     tiles of a slot hold the same value)
  *   coef    [min(max_batch, launch slot limit), H_v, 2 L]  fp32   replay coefficients of
  *                                                     one launch (replay_split only; else 0 B);
- *                                                     transient, reused launch after launch
+ *                                                     transient, reused launch after launch;
+ *                                                     may be NULL for a pool decoded only
+ *                                                     through dl_decode_step_noalloc
  * The cumulative log-decay l_bar of [DL]'s physical state is not stored: it
  * equals lamlog[n-1] when n > 0 and 0 when the log is empty. */
 typedef struct {
@@ -208,6 +210,23 @@ int dl_slot_assign(dl_pool *pool, int32_t n, const int32_t *slot_ids,
 int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
                    const void *q, const void *a_or_k, const void *b_or_v,
                    const float *lambda, const float *beta, float *out, void *stream);
+
+/* dl_decode_step for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and errors as dl_decode_step.  It allocates nothing: on a
+ * replay_split pool the ReplayPrep coefficients, the one scratch buffer of the
+ * step, go to a static device array of the library (4 MiB per GPU, held until
+ * the process ends) instead of the pool's coef buffer, which may then be NULL
+ * at dl_pool_create; on other pools, whose kernels use no scratch, it is
+ * dl_decode_step.  A launch carries at most 2^20 / (num_v_heads * 2 *
+ * merge_interval) slots (and at most dl_launch_slot_limit()); a pool with
+ * num_v_heads * 2 * merge_interval > 2^20 is refused with DL_ERR_UNSUPPORTED.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams or host threads) race and must not be issued.  The
+ * current device must be the one the pool and the stream belong to. */
+int dl_decode_step_noalloc(dl_pool *pool, int32_t B, const int32_t *slot_ids,
+                           const void *q, const void *a_or_k, const void *b_or_v,
+                           const float *lambda, const float *beta, float *out, void *stream);
 
 /* W consecutive decode steps of the same B slots in one launch, with the
  * state held on chip across them ([DL] Eq. 3 applied W times; [FPGA]'s

@@ -18,10 +18,10 @@ import numpy as np
 from . import _native as N
 from ._native import DeltaLogError, DL_DECAY, DL_DTYPE, DL_UPDATE  # noqa: F401
 
-__all__ = ["dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
-           "dl_decode_step", "dl_decode_window", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
-           "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error", "dl_launch_slot_limit",
-           "make_desc", "DeltaLogPool", "DeltaLogError"]
+__all__ = ["dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign", "dl_decode_step",
+           "dl_decode_step_noalloc", "dl_decode_window", "dl_eager_step", "dl_merge", "dl_flush_all",
+           "dl_get_log_len", "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error",
+           "dl_launch_slot_limit", "make_desc", "DeltaLogPool", "DeltaLogError"]
 
 
 def make_desc(num_slots: int, max_batch: int, H_v: int, H_k: int, d: int, L: int,
@@ -68,6 +68,12 @@ def dl_decode_step(pool: int, slot_ids, q, a_or_k, b_or_v, lam, beta, out, strea
     ids = _ids(slot_ids)
     N.check(N.lib().dl_decode_step(pool, len(ids), _i32p(ids), N.ptr(q), N.ptr(a_or_k), N.ptr(b_or_v),
                                    N.ptr(lam), N.ptr(beta), N.ptr(out), stream), "dl_decode_step")
+
+
+def dl_decode_step_noalloc(pool: int, slot_ids, q, a_or_k, b_or_v, lam, beta, out, stream) -> None:
+    ids = _ids(slot_ids)
+    N.check(N.lib().dl_decode_step_noalloc(pool, len(ids), _i32p(ids), N.ptr(q), N.ptr(a_or_k), N.ptr(b_or_v),
+                                           N.ptr(lam), N.ptr(beta), N.ptr(out), stream), "dl_decode_step_noalloc")
 
 
 def dl_decode_window(pool: int, slot_ids, W: int, q, a_or_k, b_or_v, lam, beta, out, stream) -> None:
@@ -143,7 +149,7 @@ class DeltaLogPool:
     def __init__(self, num_slots: int, H_v: int, H_k: int, d: int, L: int, decay: str,
                  update: str, state_dtype: str = "f32", in_dtype: str = "f32",
                  max_batch: Optional[int] = None, device="cuda", value_tile: int = 0,
-                 replay_split: bool = False):
+                 replay_split: bool = False, coef_buffer: bool = True):
         self.num_slots, self.H_v, self.H_k, self.d, self.L = num_slots, H_v, H_k, d, L
         self.decay, self.update = decay, update
         self.state_dtype, self.in_dtype = state_dtype, in_dtype
@@ -163,6 +169,8 @@ class DeltaLogPool:
         self._torch = torch
         ptrs = []
         for name, nbytes in zip(N.BUF_NAMES, self.sizes):
+            if name == "coef" and not coef_buffer:
+                nbytes = 0                  # decoded through dl_decode_step_noalloc only
             t = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
             self.bufs[name] = t
             ptrs.append(t.data_ptr() if nbytes else None)
@@ -238,6 +246,14 @@ class DeltaLogPool:
         ids = _ids(slot_ids)
         q, a_or_k, b_or_v, lam, beta, out = self._token_args(ids, q, a_or_k, b_or_v, lam, beta, out)
         dl_decode_step(self.handle, ids, q, a_or_k, b_or_v, lam, beta, out, self._stream())
+        return out
+
+    def decode_step_noalloc(self, slot_ids, q=None, a_or_k=None, b_or_v=None, lam=None, beta=None, out=None):
+        """decode_step through the entry point that allocates nothing (the
+        library's static scratch holds the split-replay coefficients)."""
+        ids = _ids(slot_ids)
+        q, a_or_k, b_or_v, lam, beta, out = self._token_args(ids, q, a_or_k, b_or_v, lam, beta, out)
+        dl_decode_step_noalloc(self.handle, ids, q, a_or_k, b_or_v, lam, beta, out, self._stream())
         return out
 
     def decode_window(self, slot_ids, W: int, q=None, a_or_k=None, b_or_v=None, lam=None, beta=None, out=None):

@@ -30,7 +30,7 @@ BUF_NAMES = ("base", "klog", "ulog", "lamlog", "nlog", "coef")
 EXPORTED = ("dl_pool_sizes", "dl_pool_create", "dl_pool_destroy", "dl_slot_assign",
             "dl_decode_step", "dl_eager_step", "dl_merge", "dl_flush_all", "dl_get_log_len",
             "dl_schedule", "dl_read_log_len_device", "dl_value_tile", "dl_last_error",
-            "dl_launch_slot_limit", "dl_read_base", "dl_decode_window")
+            "dl_launch_slot_limit", "dl_read_base", "dl_decode_window", "dl_decode_step_noalloc")
 
 
 class dl_pool_desc(ctypes.Structure):
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
                                    c_void_p, c_void_p, c_void_p, c_void_p]),
         "dl_eager_step": (c_int, [c_void_p, c_int32, i32p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
+        "dl_decode_step_noalloc": (c_int, [c_void_p, c_int32, i32p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p]),
         "dl_decode_window": (c_int, [c_void_p, c_int32, i32p, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p]),
         "dl_merge": (c_int, [c_void_p, c_int32, i32p, c_void_p]),

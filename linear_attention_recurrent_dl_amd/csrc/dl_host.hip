@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -254,9 +255,12 @@ int copy_states(dl_pool *pool, int32_t n, const int32_t *ids, void *ext, bool to
     return dl::launch_chunks(n, dl::kMaxLaunchSlots, launch, commit);
 }
 
-// Shared by dl_decode_step and dl_eager_step.
+// Shared by dl_decode_step, dl_eager_step and dl_decode_step_noalloc.  The
+// split-replay coefficients of a launch go to `coef` (the pool's buffer, or
+// the static scratch), launches carry at most `chunk` slots.
 int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const void *a_or_k, const void *b_or_v,
-           const float *lambda, const float *beta, float *out, void *stream, bool eager_call) {
+           const float *lambda, const float *beta, float *out, void *stream, bool eager_call,
+           float *coef = nullptr, int32_t chunk = dl::kMaxLaunchSlots) {
     if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
     const dl_pool_desc &d = pool->desc;
     if (eager_call && d.merge_interval != 1)
@@ -279,6 +283,10 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         const size_t D = d.d_k, Hv = d.num_v_heads, Hk = d.num_k_heads, s_in = dtype_size(d.in_dtype);
         const size_t lam_w = d.decay == DL_DECAY_PER_KEY ? D : 1;
         const size_t shmem = dl::log_stage_bytes(d.d_k, pool->bv, C, d.decay, d.update, d.in_dtype);
+        if (!coef) coef = pool->buf.coef;
+        if (split && !coef)
+            return fail(DL_ERR_INVALID_ARG, "split-replay pool created without a coefficient buffer: "
+                                            "decode it with dl_decode_step_noalloc");
         // A launch recorded into a graph may be replayed at any phase of the
         // append-merge cycle, so it carries no live lengths from the host.
         const bool cap = capturing(pool, stream);
@@ -289,7 +297,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
         p.ulog = pool->buf.ulog;
         p.lamlog = pool->buf.lamlog;
         p.nlog = pool->buf.nlog;
-        p.coef = pool->buf.coef;
+        p.coef = coef;
         p.H_v = d.num_v_heads;
         p.H_k = d.num_k_heads;
         p.C = C;
@@ -320,7 +328,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
             return DL_OK;
         };
         auto commit = [&](int32_t lo, int32_t cnt) { dl::mirror_decode(pool->n.data(), ids + lo, cnt, C); };
-        rc = dl::launch_chunks(B, dl::kMaxLaunchSlots, launch, commit);
+        rc = dl::launch_chunks(B, chunk, launch, commit);
         return rc ? rc : ok();
     }
     dl::mirror_decode(pool->n.data(), ids, B, d.merge_interval - 1);
@@ -382,7 +390,10 @@ int dl_pool_create(const dl_pool_desc *desc, const dl_pool_buffers *buffers, dl_
         const void *ptrs[DL_NUM_BUFS] = {buffers->base, buffers->klog, buffers->ulog, buffers->lamlog, buffers->nlog,
                                          buffers->coef};
         for (int i = 0; i < DL_NUM_BUFS; ++i) {
-            if (sz[i] && !ptrs[i]) return fail(DL_ERR_INVALID_ARG, "buffer %d is NULL but needs %zu bytes", i, sz[i]);
+            // the coefficient scratch may be left out: such a pool decodes
+            // through dl_decode_step_noalloc, whose scratch is the library's
+            if (sz[i] && !ptrs[i] && i != DL_BUF_COEF)
+                return fail(DL_ERR_INVALID_ARG, "buffer %d is NULL but needs %zu bytes", i, sz[i]);
             if ((uintptr_t)ptrs[i] & 15) return fail(DL_ERR_INVALID_ARG, "buffer %d is not 16-byte aligned", i);
         }
     }
@@ -452,6 +463,72 @@ int dl_decode_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void
 int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void *q, const void *a_or_k,
                   const void *b_or_v, const float *lambda, const float *beta, float *out, void *stream) {
     return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, true);
+}
+
+// ---- the entry point that allocates nothing -------------------------------
+//
+// Callers that cannot allocate device memory (code under graph capture, tight
+// serving loops) decode split-replay pools through dl_decode_step_noalloc: the
+// replay coefficients go to this file-scope array instead of the pool's
+// coefficient buffer.  Each GPU holds its own copy from the library's load
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not a device address: its device address is looked up once per device and
+// only that pointer is handed to kernels.
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kScratchFloats = size_t(1) << 20;          // 4 MiB per device
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's `scratch`, looked up on the first
+// call made with that device current.
+int scratch_address(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DL_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev,
+                                                  kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return DL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dl_decode_step_noalloc(dl_pool *pool, int32_t B, const int32_t *slot_ids, const void *q, const void *a_or_k,
+                           const void *b_or_v, const float *lambda, const float *beta, float *out, void *stream) {
+    if (!pool) return fail(DL_ERR_INVALID_ARG, "pool is NULL");
+    const dl_pool_desc &d = pool->desc;
+    const int C = d.merge_interval - 1;
+    if (!(d.replay_split && C > 0))            // no kernel of this pool uses a scratch buffer
+        return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, false);
+    // one slot's coefficients: 2 (C + 1) floats per v-head; a launch carries
+    // as many slots as the scratch holds (at most the usual launch limit)
+    const size_t per_slot = (size_t)d.num_v_heads * 2 * (C + 1);
+    if (per_slot > kScratchFloats)
+        return fail(DL_ERR_UNSUPPORTED, "one slot's replay coefficients need %zu floats, more than the %zu of the "
+                                        "static scratch (num_v_heads * 2 * merge_interval <= %zu)",
+                    per_slot, kScratchFloats, kScratchFloats);
+    const int32_t chunk = (int32_t)std::min<size_t>(dl::kMaxLaunchSlots, kScratchFloats / per_slot);
+    float *ptr = nullptr;
+    if (!pool->dry) {
+        const int rc = scratch_address(&ptr);
+        if (rc) return rc;
+    }
+    return decode(pool, B, slot_ids, q, a_or_k, b_or_v, lambda, beta, out, stream, false, ptr, chunk);
 }
 
 int dl_decode_window(dl_pool *pool, int32_t B, const int32_t *slot_ids, int32_t W, const void *q,
