@@ -347,9 +347,20 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
 
+    // Every kernel argument the block reads, fetched at once: left to itself
+    // the compiler loads them one by one where first used, each scalar load
+    // waited for before the next, a chain of round trips ahead of the first
+    // HBM access.  The block count comes from the arguments, not from the
+    // dispatch packet's hidden arguments, which sit in another cache line.
+    // (bf16 states: the earlier loads cost the whole-row kernels their fourth
+    // wave per SIMD, 130 instead of 128 VGPRs, so they keep the lazy order.)
+    if constexpr (sizeof(ST) == 4)
+        asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
+                     "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(p.H_v), "s"(p.H_k), "s"(p.C),
+                     "s"(p.NV), "s"(p.nunits));
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int unit = xcd_unit(blockIdx.x, p.nunits);
     const int H_v = p.H_v, C = p.C;
     const int eh = unit / NV, vt = unit - eh * NV;      // (entry, v-head), value tile
     const int e = eh / H_v, h = eh - e * H_v;
@@ -564,7 +575,7 @@ dl_step_kernel(const StepParams p) {
     }
     if constexpr (HINTED) {
         const int nd = __builtin_amdgcn_readfirstlane(n_dev);
-        if (nd != n) {                                  // the host's value is stale: stage n_dev entries
+        if (nd != n) {                           // the host's value is stale: stage n_dev entries
             __syncthreads();                            // every speculative chunk has landed
             n = min(max(nd, 0), C);
             merge = n == C;
@@ -740,6 +751,17 @@ dl_step_kernel(const StepParams p) {
 
     // ---- merge: S_bar <- e^{l'} * S_bar + sum_i Kt_i U_i^T + a b^T on this tile, from registers
     __syncthreads();
+    // 16-bit tiles: the packed tile is opaque from here, so the compiler cannot
+    // widen it to fp32 ahead of the barrier, where the projection's registers
+    // are still live (that would cost the whole-row kernels a wave per SIMD)
+    if constexpr (sizeof(ST) == 2) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            v4u32 t = __builtin_bit_cast(v4u32, tile[j]);
+            asm volatile("" : "+v"(t));
+            tile[j] = __builtin_bit_cast(uint4, t);
+        }
+    }
     float acc[RPT][VEC];
     float bcol[VEC];
 #pragma unroll
