@@ -352,12 +352,9 @@ dl_step_kernel(const StepParams p) {
     // waited for before the next, a chain of round trips ahead of the first
     // HBM access.  The block count comes from the arguments, not from the
     // dispatch packet's hidden arguments, which sit in another cache line.
-    // (bf16 states: the earlier loads cost the whole-row kernels their fourth
-    // wave per SIMD, 130 instead of 128 VGPRs, so they keep the lazy order.)
-    if constexpr (sizeof(ST) == 4)
-        asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
-                     "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(p.H_v), "s"(p.H_k), "s"(p.C),
-                     "s"(p.NV), "s"(p.nunits));
+    asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
+                 "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(p.H_v), "s"(p.H_k), "s"(p.C),
+                 "s"(p.NV), "s"(p.nunits));
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int unit = xcd_unit(blockIdx.x, p.nunits);

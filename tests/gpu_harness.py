@@ -60,6 +60,11 @@ class Result:
     compared_outputs: int = 0      # output values compared with the oracle
     expected_outputs: int = 0      # decoded entries of tracked slots x H_v x d
     compared_states: int = 0       # final-state values compared
+    # the same errors per tracked (slot, v-head): rel-L2 of all its outputs,
+    # of its final state, and the largest rel-L2 of one output vector o_t
+    out_err_slot_head_max: float = 0.0
+    state_err_slot_head_max: float = 0.0
+    out_err_vector_max: float = 0.0
     extra: Dict[str, float] = field(default_factory=dict)
 
 
@@ -90,6 +95,9 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
 
     res = Result()
     out_e = RelL2()
+    sh_num = np.zeros((len(track), Hv))            # per (tracked slot, v-head) squared error / norm
+    sh_den = np.zeros((len(track), Hv))
+    trow = {s: i for i, s in enumerate(track)}
     tracked = set(track)
     klog_written: Dict[int, Dict[int, np.ndarray]] = {s: {} for s in track}
     descs = wl.plan(steps)
@@ -118,6 +126,14 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
         if len(sel):
             o_gpu = out[torch.from_numpy(sel).to(DEV)].cpu().numpy()
             out_e.add(o_gpu, o_ref)
+            d2 = np.sum((o_gpu.astype(np.float64) - o_ref) ** 2, axis=-1)      # [n, H_v]
+            r2 = np.sum(o_ref ** 2, axis=-1)
+            rows = [trow[int(ids[e])] for e in sel]
+            np.add.at(sh_num, rows, d2)
+            np.add.at(sh_den, rows, r2)
+            nz = r2 > 0
+            if np.any(nz):
+                res.out_err_vector_max = max(res.out_err_vector_max, float(np.sqrt(np.max(d2[nz] / r2[nz]))))
             if check_klog and not eager:
                 for e in sel:
                     s = int(ids[e])
@@ -148,9 +164,19 @@ def run(cfg: Config, track: Optional[Sequence[int]] = None, steps: Optional[int]
     res.counter_mismatch += int(np.sum(pool.device_log_len() != 0))
     S_gpu = pool.read_base(track).float().cpu().numpy()
     st_e = RelL2()
-    st_e.add(S_gpu, E.states())
+    S_ref = E.states()
+    st_e.add(S_gpu, S_ref)
     res.out_err, res.state_err = out_e.value, st_e.value
+    seen = sh_den > 0
+    if np.any(seen):
+        res.out_err_slot_head_max = float(np.sqrt(np.max(sh_num[seen] / sh_den[seen])))
+    s_num = np.sum((S_gpu.astype(np.float64) - S_ref) ** 2, axis=(2, 3))
+    s_den = np.sum(S_ref ** 2, axis=(2, 3))
+    if np.any(s_den > 0):
+        res.state_err_slot_head_max = float(np.sqrt(np.max(s_num[s_den > 0] / s_den[s_den > 0])))
     res.compared_outputs, res.compared_states = out_e.count, st_e.count
+    say(f"[gpu]   per (slot, head) max: out rel-L2 {res.out_err_slot_head_max:.3e}  state rel-L2 "
+        f"{res.state_err_slot_head_max:.3e}; largest single-output rel-L2 {res.out_err_vector_max:.3e}")
     say(f"[gpu]   out rel-L2 {res.out_err:.3e}  state rel-L2 {res.state_err:.3e}  "
         f"merges {res.merges} appends {res.appends}  sched-mismatch {res.sched_mismatch}  "
         f"counter-mismatch {res.counter_mismatch}  klog-mismatch {res.klog_mismatch}")

@@ -11,6 +11,6 @@ representable in the workload's storage dtype (bf16 values are rounded to
 nearest-even from float32 here), so both sides consume identical numbers.
 """
 
-from .configs import (CONFIGS, SWEEP_OPERATORS, Config, get_config, headline_gdn,  # noqa: F401
+from .configs import (CONFIGS, SWEEP_OPERATORS, Config, at_batch, get_config, headline_gdn,  # noqa: F401
                       merge_sweep_config, small_variant)
 from .gen import StepDesc, StepInputs, Workload, round_to_bf16  # noqa: F401

@@ -124,6 +124,14 @@ def headline_gdn(batch: int, L: int = 16, steps: int = 256, seed: int = 1100) ->
                                seed=seed + batch)
 
 
+def at_batch(cfg: Config, batch: int, steps: Optional[int] = None) -> Config:
+    """A fixed-slot workload (configs 3 and 4) at another batch: B slots, all
+    decoded every step, same operator, dtypes and distributions."""
+    return dataclasses.replace(cfg, index=cfg.index * 1000 + batch,
+                               name=cfg.name.replace(f"_b{cfg.batch}_", f"_b{batch}_"), num_slots=batch,
+                               batch=batch, steps=cfg.steps if steps is None else steps, seed=cfg.seed + batch)
+
+
 SWEEP_OPERATORS = ("plain", "gdn", "gla", "kda")
 
 
