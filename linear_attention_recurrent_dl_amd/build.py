@@ -37,8 +37,11 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list:
+    # kernarg preload: the decode kernel's leading scalar arguments (launch
+    # geometry) arrive in registers, no scalar load ahead of its first fetch
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=4",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

@@ -306,7 +306,7 @@ __device__ __forceinline__ void replay_coefficients(int tid, int n, bool merge, 
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
-dl_step_kernel(const StepParams p) {
+dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const int32_t C, const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
@@ -347,26 +347,28 @@ dl_step_kernel(const StepParams p) {
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
 
-    // Every kernel argument the block reads, fetched at once: left to itself
-    // the compiler loads them one by one where first used, each scalar load
-    // waited for before the next, a chain of round trips ahead of the first
-    // HBM access.  The block count comes from the arguments, not from the
-    // dispatch packet's hidden arguments, which sit in another cache line.
-    asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
-                 "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(p.H_v), "s"(p.H_k), "s"(p.C),
-                 "s"(p.NV), "s"(p.nunits));
+    // The launch geometry comes as leading scalar arguments (block count, head
+    // counts, log capacity), which the build preloads into registers before
+    // the block starts, so the block's slot word can be fetched at once.  The
+    // block count is not read from the dispatch packet's hidden arguments,
+    // which sit in another cache line.
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int unit = xcd_unit(blockIdx.x, p.nunits);
-    const int H_v = p.H_v, C = p.C;
+    const int unit = xcd_unit(blockIdx.x, nunits);
     const int eh = unit / NV, vt = unit - eh * NV;      // (entry, v-head), value tile
     const int e = eh / H_v, h = eh - e * H_v;
     const int c0 = vt * BV;                             // first column of the tile
-    const int grp = H_v / p.H_k, g = h / grp;
+    const int grp = H_v / H_k, g = h / grp;
     const uint32_t sword = p.slots[e];
+    // Every other argument the block reads is fetched now, with the slot
+    // word, in one batch: left to itself the compiler loads each where first
+    // used and waits for it before the next, a chain of round trips ahead of
+    // the first HBM access.
+    asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
+                 "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(sword));
     const int slot = (int)(sword & kSlotMask);
     const size_t sh = (size_t)slot * H_v + h;           // slot-head index
-    const size_t gk = (size_t)slot * p.H_k + g;         // slot-(q/k head) index
+    const size_t gk = (size_t)slot * H_k + g;           // slot-(q/k head) index
     const int cg = tid % CG, rg = tid / CG;
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
@@ -403,7 +405,7 @@ dl_step_kernel(const StepParams p) {
     IT kraw{};
     if (tid < D) {
         if constexpr (TOKEN) {
-            const size_t qo = ((size_t)e * p.H_k + g) * D + tid;
+            const size_t qo = ((size_t)e * H_k + g) * D + tid;
             qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
             kraw = reinterpret_cast<const IT *>(p.k)[qo];
             kv = to_f32(kraw);
@@ -424,7 +426,7 @@ dl_step_kernel(const StepParams p) {
     // for every chunk it stages), kept packed until used
     uint4 qpk = make_uint4(0, 0, 0, 0), apk = qpk;
     if constexpr (FC && TOKEN) {
-        const size_t qo = ((size_t)e * p.H_k + g) * D + (tid % CPE) * (16 / (int)sizeof(IT));
+        const size_t qo = ((size_t)e * H_k + g) * D + (tid % CPE) * (16 / (int)sizeof(IT));
         qpk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.q) + qo);
         apk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.k) + qo);
     }
@@ -900,16 +902,16 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     const dim3 grid(p.nunits), block(NT);
     switch (mode) {
     case MODE_STEP:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
         break;
     case MODE_EAGER:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
         break;
     case MODE_MERGE:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
         break;
     case MODE_STEP_SPLIT:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
         break;
     case MODE_REPLAY_PREP:
         dl_replay_prep_kernel<D, DECAY, DELTA, ST, IT><<<grid, block, shmem, s>>>(p);
