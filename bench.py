@@ -95,6 +95,8 @@ def parse(argv=None):
                     help="comma list of workloads whose full logs dl_flush_all materializes ('' = none)")
     ap.add_argument("--windows", default="2:16,2:64,2:256,g128:16,g128:64",
                     help="comma list of workload:W window measurements ('' = none)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming reference (a read-only kernel of each decode launch's grid and bytes)")
     ap.add_argument("--detail", default="",
                     help="also write every measured row (headline, workloads, windows, flushes, host calls) "
                          "to this JSON file")
@@ -604,6 +606,81 @@ def stream_reference(torch, mib: int = 1024, reps: int = 10):
     return {"copy_GBps": copy_gbs, "read_GBps": read_gbs, "bytes": n, "kernels": "torch copy_ / sum"}
 
 
+_PROBE = None
+
+
+def _probe_lib():
+    global _PROBE
+    if _PROBE is None:
+        path = os.path.join(ROOT, "linear_attention_recurrent_dl_amd", "libdl_stream_probe.so")
+        lib = ctypes.CDLL(path)
+        lib.dl_probe_stream_read.restype = ctypes.c_int
+        lib.dl_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_uint32, ctypes.c_void_p]
+        _PROBE = lib
+    return _PROBE
+
+
+def stream_ceiling(torch, blocks: int, threads: int, bytes_per_launch: float, rotate: int, reps: int = 5):
+    """A read-only kernel with the decode launch's grid (blocks x threads),
+    each block reading its own contiguous share of bytes_per_launch with the
+    same 16-byte non-temporal loads, over `rotate` rotated buffers like the
+    workload's pools: how fast this GPU moves those bytes in that grid with no
+    other work.  Graph of back-to-back launches, median of `reps` replays."""
+    lib = _probe_lib()
+    unit = threads * 16
+    block_bytes = int(max(unit, -(-int(bytes_per_launch / blocks) // unit) * unit))
+    total = block_bytes * blocks
+    bufs = [torch.ones(total // 4, dtype=torch.float32, device="cuda") for _ in range(rotate)]
+    dst = torch.empty(blocks * threads, dtype=torch.float32, device="cuda")
+    per = max(1, -(-64 // rotate))
+
+    def launches():
+        stream = torch.cuda.current_stream().cuda_stream
+        for _ in range(per):
+            for b in bufs:
+                rc = lib.dl_probe_stream_read(b.data_ptr(), dst.data_ptr(), blocks, threads, block_bytes, stream)
+                if rc:
+                    raise RuntimeError(f"stream probe launch failed ({rc})")
+
+    launches()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launches()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    us = float(np.median(times)) * 1e3 / (per * rotate)
+    del g, bufs, dst
+    torch.cuda.empty_cache()
+    return {"blocks": blocks, "threads": threads, "block_bytes": block_bytes, "bytes": total, "rotated": rotate,
+            "us": us, "GBps": total / (us * 1e-6) / 1e9}
+
+
+def decode_grid(cfg, value_tile: int):
+    """(blocks, threads) of one decode launch of the workload."""
+    threads = 256 if cfg.d >= 128 else (128 if cfg.d >= 64 else 64)
+    return min(cfg.batch, 512) * cfg.H_v * (cfg.d // value_tile), threads
+
+
+def attach_ceiling(row, cfg, torch, rotate):
+    """Add the streaming reference for a measured DeltaLog row: same grid,
+    same algorithmic bytes per launch."""
+    blocks, threads = decode_grid(cfg, row["value_tile"])
+    c = stream_ceiling(torch, blocks, threads, row["decode_bytes_per_launch"], rotate)
+    row["stream_ceiling"] = c
+    row["frac_of_stream_ceiling"] = row["decode_GBps"] / c["GBps"]
+    return row
+
+
 def pool_bytes(dl, c, L=None) -> int:
     return sum(dl.dl_pool_sizes(dl.make_desc(c.num_slots, c.batch, c.H_v, c.H_k, c.d, L or c.L, c.decay,
                                              c.update, c.state_dtype, c.in_dtype)))
@@ -737,6 +814,8 @@ def main(argv=None) -> int:
     r = time_workload(cfg, False, steps, warmup, a.rotate, distinct, torch, dl, native, a.value_tile,
                       graph=not a.no_graph)
     head = summarize(cfg, r, steps, "deltalog")
+    if not a.no_ceiling:
+        attach_ceiling(head, cfg, torch, a.rotate)
     print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
     eager_head = None
     if not a.no_eager:
@@ -760,6 +839,8 @@ def main(argv=None) -> int:
                                    graph=not a.no_graph)
                 s = summarize(c, rr, xs, "eager" if eager else "deltalog")
                 s["rotated_pools"] = R
+                if not eager and not a.no_ceiling:
+                    attach_ceiling(s, c, torch, R)
                 s["pool_bytes"] = ws if not eager else sum(dl.dl_pool_sizes(dl.make_desc(
                     c.num_slots, c.batch, c.H_v, c.H_k, c.d, 1, c.decay, c.update, c.state_dtype, c.in_dtype)))
                 extras.append(s)
@@ -849,6 +930,9 @@ def compact_rows(extras) -> list:
         else:
             row.update({"tile": s["value_tile"], "us": _r(s["decode_launch_us"], 2), "GBps": _r(s["decode_GBps"], 0),
                         "frac": _r(s["decode_frac_of_8TBps"], 3), "Mhs": _r(s["head_steps_per_s"] / 1e6, 2)})
+            if "stream_ceiling" in s:
+                row["ceil_GBps"] = _r(s["stream_ceiling"]["GBps"], 0)
+                row["of_ceil"] = _r(s["frac_of_stream_ceiling"], 3)
     for row in rows:
         if row.get("us") and row.get("eager_us"):
             row["x_eager"] = _r(row["eager_us"] / row["us"], 3)
@@ -885,7 +969,8 @@ def make_line(cfg, rotate, steps, warmup, steps_requested, head, eager_head, ext
                      "kernel": "dl_step_kernel (decode, append/merge)",
                      "bytes_per_launch": _r(head["decode_bytes_per_launch"], 1),
                      "launch_us": _r(head["decode_launch_us"], 3),
-                     "launch_source": head["decode_launch_source"]},
+                     "launch_source": head["decode_launch_source"],
+                     "stream_ceiling_GBps": _r(head.get("stream_ceiling", {}).get("GBps"), 1)},
         "cpu_baseline": None if cpu is None else {
             "value": _r(cpu["value"], 1), "unit": cpu["unit"], "cores": cpu["cores"], "kind": cpu["kind"],
             "sample": cpu["sample"]},

@@ -80,6 +80,23 @@ def _compile(src: str, extra: list) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libdl_stream_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The benchmark's streaming reference kernel, a library of its own."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + compile_flags() + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"[build] {PROBE_LIB}", flush=True)
+    return PROBE_LIB
+
+
 def build(jobs: int = 0, extra: list = None, verbose: bool = True) -> str:
     extra = list(extra or []) + os.environ.get("DL_EXTRA_CFLAGS", "").split()
     os.makedirs(BUILD, exist_ok=True)
@@ -96,6 +113,7 @@ def build(jobs: int = 0, extra: list = None, verbose: bool = True) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"[build] {LIB_PATH} ({len(srcs)} sources, {time.time() - t0:.1f}s)", flush=True)
+    build_probe(verbose)
     return LIB_PATH
 
 

@@ -2,7 +2,7 @@
 
     python -m linear_attention_recurrent_dl_amd.rocprof_summary trace  <results.db | kernel_trace.csv>
     python -m linear_attention_recurrent_dl_amd.rocprof_summary pmc    <results.db | counter_collection.csv> COUNTER
-    python -m linear_attention_recurrent_dl_amd.rocprof_summary traffic FETCH_DB WRITE_DB KERNEL_SUBSTR COPY_BYTES [OUT.json]
+    python -m linear_attention_recurrent_dl_amd.rocprof_summary traffic FETCH_DB WRITE_DB KERNEL_SUBSTR COPY_BYTES [OUT.json|-] [LAST_N]
     python -m linear_attention_recurrent_dl_amd.rocprof_summary tail   <kernel_trace.csv> KERNEL_SUBSTR N
 
 ``trace`` prints count / average / min / max duration per kernel name;
@@ -12,7 +12,7 @@ WRITE_SIZE run into HBM bytes per launch of the kernel whose name contains
 KERNEL_SUBSTR: each counter (KiB per dispatch) is scaled by the factor that
 maps the same counter of a plain device copy of COPY_BYTES bytes (the largest
 copy kernel in the run, which reads and writes COPY_BYTES each) onto its known
-size.  ``tail`` splits the dispatches of the kernel whose name contains
+size, over all its dispatches or its last LAST_N (CSV input).  ``tail`` splits the dispatches of the kernel whose name contains
 KERNEL_SUBSTR, in start order, into all but the last N and the last N, and
 prints count and average duration of each part and the median start-to-start
 period of the last N (a timed graph replay is the last dispatches of a run).
@@ -85,6 +85,16 @@ def pmc_dispatches(path: str, counter: str):
     return {n: list(d.values()) for n, d in per.items()}
 
 
+def _pmc_by_dispatch(path: str, counter: str):
+    """{kernel name: {dispatch id: value of COUNTER}} (CSV output)."""
+    per = defaultdict(lambda: defaultdict(float))
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return per
+
+
 def pmc_rows(path: str, counter: str):
     """[(name, dispatches, avg value per dispatch)]."""
     per = defaultdict(lambda: defaultdict(float))     # name -> dispatch -> value
@@ -126,9 +136,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int) -> dict:
-    f_rows = pmc_rows(fetch_path, "FETCH_SIZE")
-    w_rows = pmc_rows(write_path, "WRITE_SIZE")
+def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int, last: int = 0) -> dict:
+    """HBM bytes per launch of the kernel matching `kernel` (most dispatches),
+    averaged over all its dispatches or, with last > 0, over its last `last`
+    dispatches (the timed steps, after set-up and warm-up launches)."""
+
+    def rows_of(path, counter):
+        if not last:
+            return pmc_rows(path, counter)
+        per = defaultdict(dict)
+        for name, did_vals in _pmc_by_dispatch(path, counter).items():
+            ids = sorted(did_vals, key=lambda x: int(x))[-last:]
+            per[name] = [did_vals[i] for i in ids]
+        return [(n, len(v), sum(v) / len(v)) for n, v in per.items()]
+
+    f_rows = rows_of(fetch_path, "FETCH_SIZE")
+    w_rows = rows_of(write_path, "WRITE_SIZE")
 
     def pick(rows, sub):
         m = [r for r in rows if sub in r[0]]
@@ -183,10 +206,12 @@ def main(argv=None) -> int:
         print(f"last {nt} dispatches: avg {at / 1e3:.3f} us, median start-to-start {pt / 1e3:.3f} us")
     elif mode == "traffic":
         import json
-        t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
+        last = int(argv[6]) if len(argv) > 6 else 0
+        t = traffic(argv[1], argv[2], argv[3], int(argv[4]), last)
+        t["dispatches_averaged"] = "last %d" % last if last else "all"
         txt = json.dumps(t, indent=1)
         print(txt)
-        if len(argv) > 5:
+        if len(argv) > 5 and argv[5] != "-":
             with open(argv[5], "w") as f:
                 f.write(txt + "\n")
     else:

@@ -52,10 +52,12 @@ def _synthetic_rows():
     """Measured rows shaped as bench.summarize / time_window / time_flush give them."""
     from workloads import CONFIGS
     head = {"workload": "gdn_b1_h32_d128", "kernel": "deltalog", "batch": 1, "state": "f32", "value_tile": 16,
+            "stream_ceiling": {"GBps": 1234.5678}, "frac_of_stream_ceiling": 0.55,
             "head_steps_per_s": 8.75e6, "tokens_per_s": 2.73e5, "ms_per_step": 3.66e-3, "decode_GBps": 680.1,
             "decode_frac_of_8TBps": 0.085, "decode_bytes_per_launch": 2.49e6, "decode_launch_us": 3.66,
             "decode_launch_source": "graph replay, back-to-back launches"}
     eager = dict(head, kernel="eager", ms_per_step=3.0e-3, head_steps_per_s=1.07e7, decode_GBps=1400.0)
+    eager.pop("stream_ceiling")
     extras = []
     for tag in ("1", "3", "4", "5", "5tp8", "g64", "g128", "g256", "g512"):
         c = bench.extra_cfg(tag)
@@ -63,7 +65,9 @@ def _synthetic_rows():
             extras.append({"workload": c.name, "kernel": k, "batch": c.batch, "state": c.state_dtype,
                            "value_tile": 128, "decode_launch_us": us, "decode_GBps": 5712.345678,
                            "decode_frac_of_8TBps": 0.714043, "head_steps_per_s": 1.234567e8, "rotated_pools": 4,
-                           "long_field_that_stays_in_the_detail": "x" * 500})
+                           "long_field_that_stays_in_the_detail": "x" * 500,
+                           "stream_ceiling": {"GBps": 6234.56789, "us": 40.1234, "blocks": 8192},
+                           "frac_of_stream_ceiling": 0.9162345})
     windows = [{"workload": "gdn_b1_h32_d128", "W": w, "us_per_step": 0.71, "speedup_per_step_vs_decode": 5.1}
                for w in (16, 64, 256)]
     flushes = [{"workload": "gdn_b256_h32_d128", "launch_us": 205.9, "frac_of_8TBps": 0.71}]
@@ -91,7 +95,15 @@ def test_stdout_line_is_compact_and_parses():
     assert set(back["cpu_baseline"]) == {"value", "unit", "cores", "kind", "sample"}
     names = [w["w"] for w in back["workloads"]]
     assert len(names) == 9 and len(set(names)) == 9
-    assert all("x_eager" in w and "frac" in w for w in back["workloads"])
+    assert all("x_eager" in w and "frac" in w and "of_ceil" in w for w in back["workloads"])
+
+
+def test_decode_grid_matches_the_launch():
+    from workloads import CONFIGS
+    assert bench.decode_grid(CONFIGS[2], 16) == (256, 256)
+    assert bench.decode_grid(CONFIGS[3], 64) == (2048, 128)
+    assert bench.decode_grid(CONFIGS[5], 128) == (8192, 256)
+    assert bench.decode_grid(CONFIGS[1], 16) == (2, 64)
 
 
 def test_line_dtype_names_the_storage_of_16_bit_workloads():
