@@ -39,8 +39,10 @@ KDA-style), with the eager kernel (M = 1) as reference, on cold rotated pools.
 ``--sweep state`` decodes one pool of 128 MiB to 1 GiB (B = 64 .. 512, d = 128,
 fp32) per family (GDN, KDA-style, GLA-style) without rotation, DeltaLog and
 eager, so that the Infinity Cache shows.  ``--sweep split`` compares fused
-replay with split ReplayPrep by batch and value-tile width.  Each
-prints one JSON line of rows instead of the headline line.
+replay with split ReplayPrep by batch and value-tile width.  ``--sweep stream``
+times the read-only streaming reference over grid shapes (one round of blocks
+against several rounds).  Each prints one JSON line of rows instead of the
+headline line.
 """
 
 from __future__ import annotations
@@ -102,8 +104,9 @@ def parse(argv=None):
     ap.add_argument("--detail", default="",
                     help="also write every measured row (headline, workloads, windows, flushes, host calls) "
                          "to this JSON file")
-    ap.add_argument("--sweep", choices=["merge", "state", "split"], default=None,
-                    help="merge-interval, state-size or split-replay sweep instead of the headline line")
+    ap.add_argument("--sweep", choices=["merge", "state", "split", "stream"], default=None,
+                    help="merge-interval, state-size, split-replay or streaming-reference sweep instead of the "
+                         "headline line")
     return ap.parse_args(argv)
 
 
@@ -749,6 +752,19 @@ def run_sweep(kind, a, torch, dl, native) -> dict:
                                op=op, B_V=bv)
                     sp["split_vs_fused"] = fu["decode_launch_us"] / sp["decode_launch_us"]
                     rows += [fu, sp]
+    elif kind == "stream":
+        # the read-only reference kernel over grid shapes: one round of blocks
+        # against several rounds, at the decode launches' block sizes
+        shapes = [(2048, 128, 16 << 10), (2048, 128, 24 << 10), (4096, 128, 24 << 10), (8192, 128, 24 << 10),
+                  (256, 256, 8 << 10), (2048, 256, 72 << 10), (4096, 256, 72 << 10), (8192, 256, 72 << 10),
+                  (8192, 256, 40 << 10), (16384, 256, 256 << 10)]
+        for blocks, threads, bb in shapes:
+            total = blocks * bb
+            R = 1 if total >= a.rotate_bytes else int(np.ceil(a.rotate_bytes / total))
+            c = stream_ceiling(torch, blocks, threads, blocks * bb, R)
+            c["frac_of_8TBps"] = c["GBps"] / PEAK_HBM_GBS
+            print(f"[sweep] {json.dumps(c)}", file=sys.stderr, flush=True)
+            rows.append(c)
     else:
         for op in ("gdn", "kda", "gla"):
             for B in (64, 128, 256, 512):

@@ -2,7 +2,8 @@
 // kernel that only reads, with the decode launch's grid shape.  Each of the
 // `blocks` blocks of `threads` threads reads its own contiguous run of
 // `block_bytes` bytes (a multiple of threads * 16) with 16-byte non-temporal
-// loads, as the decode kernel reads its tile, folds them into one value per
+// loads, up to 16 in flight per thread (as the decode kernel issues its tile
+// and log loads before using any), folds them into one value per
 // thread and stores it, so no load can be dropped.  Timed next to a decode
 // launch of the same blocks and bytes, it shows how fast this GPU moves that
 // many bytes in that grid when nothing else is done.
@@ -15,22 +16,22 @@ typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 template <int NT>
 __global__ void __launch_bounds__(NT) stream_read_kernel(const char *src, float *dst, uint32_t block_bytes) {
+    constexpr int U = 16;                       // 16-byte loads in flight per thread
     const char *b = src + (size_t)blockIdx.x * block_bytes;
     const uint32_t loads = block_bytes / (NT * 16);
     float acc = 0.f;
-    uint32_t j = 0;
-    for (; j + 8 <= loads; j += 8) {            // eight 16-byte loads in flight per thread
-        v4u32 r[8];
+    for (uint32_t j = 0; j < loads; j += U) {   // a batch of up to U loads, all issued before any is used
+        v4u32 r[U];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            r[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(b + ((size_t)(j + u) * NT + threadIdx.x) * 16));
+        for (int u = 0; u < U; ++u) {
+            r[u] = v4u32{0u, 0u, 0u, 0u};
+            if (j + u < loads)
+                r[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4u32 *>(b + ((size_t)(j + u) * NT + threadIdx.x) * 16));
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < U; ++u)
             acc += __uint_as_float(r[u].x) + __uint_as_float(r[u].y) + __uint_as_float(r[u].z) + __uint_as_float(r[u].w);
-    }
-    for (; j < loads; ++j) {
-        const v4u32 r = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(b + ((size_t)j * NT + threadIdx.x) * 16));
-        acc += __uint_as_float(r.x) + __uint_as_float(r.y) + __uint_as_float(r.z) + __uint_as_float(r.w);
     }
     dst[(size_t)blockIdx.x * NT + threadIdx.x] = acc;
 }
