@@ -98,6 +98,9 @@ int validate_desc(const dl_pool_desc *d) {
                     dl::kMaxLogStageBytes);
     const long long units = (long long)d->max_batch * d->num_v_heads;
     if (units > (1LL << 30)) return fail(DL_ERR_INVALID_ARG, "max_batch * num_v_heads too large");
+    // the kernels index (slot, v-head, value tile) in 32 bits
+    if ((long long)d->num_slots * d->num_v_heads * (d->d_k / bv) > (1LL << 31) - 1)
+        return fail(DL_ERR_INVALID_ARG, "num_slots * num_v_heads * (d / value_tile) must be below 2^31");
     return DL_OK;
 }
 

@@ -306,7 +306,7 @@ __device__ __forceinline__ void replay_coefficients(int tid, int n, bool merge, 
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
-dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const int32_t C, const StepParams p) {
+dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gmag, const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
@@ -329,6 +329,20 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     constexpr int CPE = D / (16 / (int)sizeof(IT));   // 16-byte key chunks per log entry
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+    // Narrow tiles (B_V <= 32: small batches) of a decode launch with scalar or
+    // no decay stage the log by entries: a lane takes two adjacent key chunks
+    // of one entry, so an entry spans TPE2 = CPE / 2 lanes and one round of
+    // the block covers EPR entries (16 at d = 128 with fp32 keys), while the
+    // value-factor chunks go to lanes of their own.  Against chunk rounds over
+    // the whole log this halves the lanes each replay dot product is summed
+    // over, needs one round for a log of up to EPR entries, and leaves no lane
+    // choosing between log arrays.  Each lane's instructions count at batch 1,
+    // where a block has its CU to itself and a wave issues one instruction
+    // per four cycles.
+    constexpr bool SMALL = HINTED && FC && BV <= 32 && CPE >= 2;
+    constexpr int TPE2 = SMALL ? CPE / 2 : 1;         // lanes per log entry (narrow tiles)
+    constexpr int EPR = NT / TPE2;                    // log entries per round (narrow tiles)
+    constexpr int QP = SMALL ? 2 : 1;                 // key chunks of q and a per lane
     static_assert(BV % UV == 0, "value-factor chunks");
 
     __shared__ float s_q[D];        // e^{l'} * q
@@ -347,18 +361,27 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     __shared__ float s_s;           // a . q
     extern __shared__ float4 s_dyn[];
 
-    // The launch geometry comes as leading scalar arguments (block count, head
-    // counts, log capacity), which the build preloads into registers before
-    // the block starts, so the block's slot word can be fetched at once.  The
-    // block count is not read from the dispatch packet's hidden arguments,
-    // which sit in another cache line.
+    // The launch geometry comes as leading scalar arguments (head counts, log
+    // capacity, the q/k-head divisor), which the build preloads into registers
+    // before the block starts, so the block's slot word can be fetched at
+    // once.  The grid has one row per batch entry (blockIdx.y); along x run
+    // the entry's (v-head, value tile) units, numbered so that each XCD holds
+    // a contiguous run of them.  No integer division: a wave issues one
+    // instruction per four cycles, and a division by a run-time value costs
+    // about 25 of them ahead of the first load.  The q/k head of v-head h is
+    // h / (H_v / H_k), taken as the high word of h * gmag with
+    // gmag = ceil(2^32 / (H_v / H_k)) (exact for h < 2^16), or h when gmag = 0
+    // (one v-head per q/k head).
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int unit = xcd_unit(blockIdx.x, nunits);
-    const int eh = unit / NV, vt = unit - eh * NV;      // (entry, v-head), value tile
-    const int e = eh / H_v, h = eh - e * H_v;
+    const int ux = xcd_unit(blockIdx.x, H_v * NV);
+    const int e = blockIdx.y;                           // batch entry of this launch
+    const int h = ux / NV, vt = ux - h * NV;            // v-head, value tile
+    const int eh = e * H_v + h;                         // (entry, v-head)
     const int c0 = vt * BV;                             // first column of the tile
-    const int grp = H_v / H_k, g = h / grp;
+    const int g = gmag ? (int)__umulhi((uint32_t)h, gmag) : h;
+    // the first v-head of its q/k group writes the group's key factor
+    const bool kwriter = h == 0 || gmag == 0 || (int)__umulhi((uint32_t)(h - 1), gmag) != g;
     const uint32_t sword = p.slots[e];
     // Every other argument the block reads is fetched now, with the slot
     // word, in one batch: left to itself the compiler loads each where first
@@ -366,9 +389,17 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     // the first HBM access.
     asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
                  "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(sword));
-    const int slot = (int)(sword & kSlotMask);
-    const size_t sh = (size_t)slot * H_v + h;           // slot-head index
-    const size_t gk = (size_t)slot * H_k + g;           // slot-(q/k head) index
+    const uint32_t slot = sword & kSlotMask;
+    // Slot-head and slot-(q/k head) indices.  The host keeps P * H_v * N_V
+    // below 2^31, so they and the (slot-head, tile) index fit 32 bits, and
+    // each 64-bit offset below comes from one 32 x 32-bit product.
+    const uint32_t sh32 = slot * (uint32_t)H_v + (uint32_t)h;
+    const uint32_t gk32 = slot * (uint32_t)H_k + (uint32_t)g;
+    const uint32_t shv = sh32 * NV + (uint32_t)vt;      // (slot-head, value tile): counter, base tile
+    const size_t shC = (size_t)sh32 * (uint32_t)C;      // its first log entry
+    const size_t gkC = (size_t)gk32 * (uint32_t)C;      // the q/k head's first key-log entry
+    const uint32_t ek = (uint32_t)e * H_k + g;          // token row of q, k
+    const uint32_t ev = (uint32_t)eh;                   // token row of v, lambda, beta, output
     const int cg = tid % CG, rg = tid / CG;
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
@@ -377,17 +408,53 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     // device counter; the counter, read alongside, decides (step 2 stages
     // again when the two differ, as after direct launches that follow a
     // graph capture).  A launch recorded into a graph carries no value and
-    // waits for the counter.  The counter's index is made opaque to keep it a
-    // vector load: a scalar one would order the scalar argument loads behind it.
-    int n = 0, n_dev = 0;
+    // waits for the counter, whose round trip the token loads below overlap.
+    // The counter is a scalar load (its index is uniform and nothing has been
+    // stored yet): the scalar path answers in about half the time of a vector
+    // load, and its wait does not hold the token loads, which a vector load's
+    // in-order count would.  The scalar cache starts every launch empty, so it
+    // sees the previous launch's store.
+    int n_dev = 0;
+    if constexpr (HINTED) n_dev = ((const __attribute__((address_space(4))) int32_t *)(size_t)p.nlog)[shv];
+
+    // ---- 1. every load of the block is issued before any is consumed: the
+    //         token inputs (while the counter is in flight), the whole live
+    //         log, then the base tile.
+    float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
+    IT kraw{};
+    if constexpr (TOKEN) {
+        if (tid < D) {
+            const uint32_t qo = ek * D + tid;
+            qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+            kraw = reinterpret_cast<const IT *>(p.k)[qo];
+            kv = to_f32(kraw);
+            if (tid < BV) vv = to_f32(reinterpret_cast<const IT *>(p.v)[ev * D + c0 + tid]);
+            if constexpr (SCALAR) lam = p.lam[ev];
+            if constexpr (PERKEY) lam = p.lam[ev * D + tid];
+            if constexpr (DELTA) beta = p.beta[ev];
+        }
+    }
+    // q and a on the keys of this thread's key chunks (the same positions for
+    // every chunk it stages), kept packed until used
+    uint4 qpk[QP], apk[QP];
+#pragma unroll
+    for (int c = 0; c < QP; ++c) qpk[c] = apk[c] = make_uint4(0, 0, 0, 0);
+    if constexpr (FC && TOKEN) {
+        const int kc = SMALL ? (tid % TPE2) * 2 : tid % CPE;    // first key chunk of the lane
+        const uint32_t qo = ek * D + kc * KV;
+#pragma unroll
+        for (int c = 0; c < QP; ++c) {
+            qpk[c] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.q) + qo + c * KV);
+            apk[c] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.k) + qo + c * KV);
+        }
+    }
+
+    int n = 0;
     if constexpr (HINTED) {
-        int ni = (int)(sh * NV + vt);
-        asm volatile("" : "+v"(ni));
-        n_dev = p.nlog[ni];
         const uint32_t hint = sword >> kSlotBits;
         n = hint == kNoHint ? min(max(__builtin_amdgcn_readfirstlane(n_dev), 0), C) : min((int)hint, C);
     } else if constexpr (LOG) {
-        n = p.nlog[sh * NV + vt];
+        n = p.nlog[shv];
     }
     if constexpr (MODE == MODE_MERGE) {
         if (n == 0) return;                             // empty log: nothing to materialize
@@ -399,36 +466,14 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
     const float *lamlog = p.lamlog;
 
-    // ---- 1. every load of the block is issued before any is consumed:
-    //         token inputs, the whole live log, then the base tile.
-    float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
-    IT kraw{};
-    if (tid < D) {
-        if constexpr (TOKEN) {
-            const size_t qo = ((size_t)e * H_k + g) * D + tid;
-            qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
-            kraw = reinterpret_cast<const IT *>(p.k)[qo];
-            kv = to_f32(kraw);
-            if (tid < BV) vv = to_f32(reinterpret_cast<const IT *>(p.v)[((size_t)e * H_v + h) * D + c0 + tid]);
-            if constexpr (SCALAR) lam = p.lam[(size_t)e * H_v + h];
-            if constexpr (PERKEY) lam = p.lam[((size_t)e * H_v + h) * D + tid];
-            if constexpr (DELTA) beta = p.beta[(size_t)e * H_v + h];
-        }
-        if (LOG && n > 0) {
-            if constexpr (SCALAR) lbar = lamlog[sh * C + (n - 1)];
-            if constexpr (PERKEY) lbar = lamlog[(sh * C + (n - 1)) * D + tid];
+    if constexpr (LOG) {
+        if (tid < D && n > 0) {
+            if constexpr (SCALAR) lbar = lamlog[shC + (n - 1)];
+            if constexpr (PERKEY) lbar = lamlog[(shC + (n - 1)) * D + tid];
         }
     }
     if constexpr (SCALAR && LOG) {
-        if (fused && tid < n) lam_i = lamlog[sh * C + tid];
-    }
-    // q and a on the KV keys of this thread's key chunks (the same positions
-    // for every chunk it stages), kept packed until used
-    uint4 qpk = make_uint4(0, 0, 0, 0), apk = qpk;
-    if constexpr (FC && TOKEN) {
-        const size_t qo = ((size_t)e * H_k + g) * D + (tid % CPE) * (16 / (int)sizeof(IT));
-        qpk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.q) + qo);
-        apk = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.k) + qo);
+        if (fused && tid < n) lam_i = lamlog[shC + tid];
     }
     // split replay: this append's coefficients from the scratch (c^q, c^k per
     // live entry, then a . q)
@@ -462,9 +507,9 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
         s_ll = reinterpret_cast<float *>(s_log + (size_t)(cK + cU) * 16);
     };
     log_layout();
-    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gk * C * D);
-    const BT *ub = ulog + sh * C * D + c0;
-    const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + sh * C * D);
+    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gkC * D);
+    const BT *ub = ulog + shC * D + c0;
+    const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + shC * D);
     auto chunk_ptr = [&](int x) -> const uint4 * {
         if (x < cK) return kb + x;
         if (x < cK + cU) {
@@ -484,8 +529,8 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     auto chunk_dots = [&](const int x, const uint4 w) {
         float pq = 0.f, pk = 0.f;
         if (x < cK) {
-            pq = dot16<IT>(w, qpk);
-            if constexpr (DELTA) pk = dot16<IT>(w, apk);
+            pq = dot16<IT>(w, qpk[0]);
+            if constexpr (DELTA) pk = dot16<IT>(w, apk[0]);
         }
         pq = group_sum<CPE>(pq);
         if constexpr (DELTA) pk = group_sum<CPE>(pk);
@@ -494,10 +539,66 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
             if constexpr (DELTA) s_ck[x / CPE] = pk;
         }
     };
+    // narrow tiles: round r of key entries (entry r EPR + tid / TPE2, two
+    // chunks per lane), staged with their raw dot products; value-factor
+    // chunks u = r NT + tid
+    auto k_load = [&](const int r, uint4 (&w)[2]) {
+        const int i = r * EPR + tid / TPE2;
+        if (i < n) {
+            const uint4 *src = kb + (size_t)i * CPE + (tid % TPE2) * 2;
+            w[0] = src[0];
+            w[1] = src[1];
+        }
+    };
+    auto k_stage = [&](const int r, const uint4 (&w)[2]) {   // every lane, uniform r (DPP sums)
+        const int i = r * EPR + tid / TPE2;
+        float pq = 0.f, pk = 0.f;
+        if (i < n) {
+            const int x = i * CPE + (tid % TPE2) * 2;
+            stage(x, w[0]);
+            stage(x + 1, w[1]);
+            pq = dot16<IT>(w[0], qpk[0]) + dot16<IT>(w[1], qpk[QP - 1]);
+            if constexpr (DELTA) pk = dot16<IT>(w[0], apk[0]) + dot16<IT>(w[1], apk[QP - 1]);
+        }
+        pq = group_sum<TPE2>(pq);
+        if constexpr (DELTA) pk = group_sum<TPE2>(pk);
+        if (i < n && tid % TPE2 == 0) {
+            s_cq[i] = pq;
+            if constexpr (DELTA) s_ck[i] = pk;
+        }
+    };
+    auto u_load = [&](const int r, uint4 &w) {
+        const int u = r * NT + tid;
+        if (u < cU) {
+            const int i = u / UCH;
+            w = *reinterpret_cast<const uint4 *>(ub + (size_t)i * D + (u - i * UCH) * UV);
+        }
+    };
+    auto u_stage = [&](const int r, const uint4 &w) {
+        const int u = r * NT + tid;
+        if (u < cU) stage(cK + u, w);
+    };
+    constexpr int RK = SMALL ? 2 : 1;                   // key rounds loaded up front (longer logs stream)
+    constexpr int RU = SMALL ? 2 : 1;                   // value-factor rounds loaded up front
+    uint4 pk[RK][2], pu[RU];
+    // (the chunk rounds past the live log are left by a uniform branch: a
+    // short log pays for the rounds it uses, not for the capacity's)
     uint4 pf[PF];
-    if constexpr (LOG) {
+    if constexpr (SMALL) {
+#pragma unroll
+        for (int r = 0; r < RK; ++r) {
+            if (r * EPR >= n) break;
+            k_load(r, pk[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < RU; ++r) {
+            if (r * NT >= cU) break;
+            u_load(r, pu[r]);
+        }
+    } else if constexpr (LOG) {
 #pragma unroll
         for (int m = 0; m < PF; ++m) {
+            if (m * NT >= ctot) break;
             const int x = tid + m * NT;
             if (x < ctot) pf[m] = *chunk_ptr(x);
         }
@@ -506,7 +607,7 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
     // overlaps its arrival.  The base is value-tile major, [slot-head][NV][D][BV],
     // so the tile is one contiguous run: a thread reads tile rows rg + RG * j,
     // columns cg * VEC ..
-    const ST *tbase = reinterpret_cast<const ST *>(p.base) + (sh * NV + vt) * (size_t)(D * BV);
+    const ST *tbase = reinterpret_cast<const ST *>(p.base) + (size_t)shv * (D * BV);
     const uint32_t toff = (uint32_t)((rg * BV + cg * VEC) * sizeof(ST));
     constexpr uint32_t TROW = RG * BV * sizeof(ST);     // bytes between a thread's rows
     uint4 tile[RPT];
@@ -544,8 +645,31 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
                 if (tid == n) s_s = s_r;
             }
         }
+        if constexpr (SMALL) {
+#pragma unroll
+            for (int r = 0; r < RK; ++r) {
+                if (r * EPR >= n) break;
+                k_stage(r, pk[r]);
+            }
+            for (int r = RK; r * EPR < n; ++r) {        // long logs
+                uint4 w[2];
+                k_load(r, w);
+                k_stage(r, w);
+            }
+#pragma unroll
+            for (int r = 0; r < RU; ++r) {
+                if (r * NT >= cU) break;
+                u_stage(r, pu[r]);
+            }
+            for (int r = RU; r * NT < cU; ++r) {
+                uint4 w;
+                u_load(r, w);
+                u_stage(r, w);
+            }
+        } else {
 #pragma unroll
         for (int m = 0; m < PF; ++m) {
+            if (m * NT >= ctot) break;
             const int x = tid + m * NT;
             if (x < ctot) stage(x, pf[m]);
             if constexpr (FC && TOKEN) {
@@ -565,11 +689,16 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
         } else {
             for (int x = tid + PF * NT; x < ctot; x += NT) stage(x, *chunk_ptr(x));   // long logs
         }
+        }
     }
     if constexpr (FC && TOKEN) {                        // a . q, summed by the first chunk group
+        constexpr int AG = SMALL ? TPE2 : CPE;          // lanes holding the D keys
         float pa = 0.f;
-        if (tid < CPE) pa = dot16<IT>(qpk, apk);
-        pa = group_sum<CPE>(pa);
+        if (tid < AG) {
+#pragma unroll
+            for (int c = 0; c < QP; ++c) pa += dot16<IT>(qpk[c], apk[c]);
+        }
+        pa = group_sum<AG>(pa);
         if (tid == 0) s_s = pa;
     }
     if constexpr (HINTED) {
@@ -582,15 +711,26 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
             if (tid < D) {
                 float lb = 0.f;
                 if (n > 0) {
-                    if constexpr (SCALAR) lb = lamlog[sh * C + (n - 1)];
-                    if constexpr (PERKEY) lb = lamlog[(sh * C + (n - 1)) * D + tid];
+                    if constexpr (SCALAR) lb = lamlog[shC + (n - 1)];
+                    if constexpr (PERKEY) lb = lamlog[(shC + (n - 1)) * D + tid];
                 }
                 stage_decay(lb);
             }
             if constexpr (SCALAR) {
-                if (tid < n) s_lam[tid] = lamlog[sh * C + tid];
+                if (tid < n) s_lam[tid] = lamlog[shC + tid];
             }
-            if constexpr (FC && TOKEN) {
+            if constexpr (SMALL) {
+                for (int r = 0; r * EPR < n; ++r) {
+                    uint4 w[2];
+                    k_load(r, w);
+                    k_stage(r, w);
+                }
+                for (int r = 0; r * NT < cU; ++r) {
+                    uint4 w;
+                    u_load(r, w);
+                    u_stage(r, w);
+                }
+            } else if constexpr (FC && TOKEN) {
                 for (int xb = 0; xb < ctot; xb += NT) {
                     const int x = xb + tid;
                     uint4 w = make_uint4(0, 0, 0, 0);
@@ -676,13 +816,13 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
         // No block of this launch reads entry n or another block's counter.
         if constexpr (LOG) {
             if (!merge && owner && tid < D) {
-                if (h % grp == 0) reinterpret_cast<IT *>(p.klog)[(gk * C + n) * D + tid] = kraw;
-                if constexpr (PERKEY) p.lamlog[(sh * C + n) * D + tid] = s_lp[tid];
+                if (kwriter) reinterpret_cast<IT *>(p.klog)[(gkC + n) * D + tid] = kraw;
+                if constexpr (PERKEY) p.lamlog[(shC + n) * D + tid] = s_lp[tid];
                 if constexpr (SCALAR) {
-                    if (tid == 0) p.lamlog[sh * C + n] = s_lp[0];
+                    if (tid == 0) p.lamlog[shC + n] = s_lp[0];
                 }
             }
-            if (tid == 0) p.nlog[sh * NV + vt] = merge ? 0 : n + 1;
+            if (tid == 0) p.nlog[shv] = merge ? 0 : n + 1;
         }
         __syncthreads();
 
@@ -736,15 +876,15 @@ dl_step_kernel(const int32_t nunits, const int32_t H_v, const int32_t H_k, const
                 for (int c = 0; c < UV; ++c) ub[c] = bc[c];
                 wu = pack_16<BT, UV>(ub);
             }
-            char *dst = is_u ? reinterpret_cast<char *>(p.ulog) + ((sh * C + n) * D + c0 + cb) * sizeof(BT)
-                             : reinterpret_cast<char *>(p.out) + (((size_t)e * H_v + h) * D + c0 + cb) * sizeof(float);
+            char *dst = is_u ? reinterpret_cast<char *>(p.ulog) + ((shC + n) * D + c0 + cb) * sizeof(BT)
+                             : reinterpret_cast<char *>(p.out) + ((size_t)ev * D + c0 + cb) * sizeof(float);
             // per-component select: a select of whole vectors goes through scratch
             st16_stream(dst, 0, make_uint4(is_u ? wu.x : wo.x, is_u ? wu.y : wo.y, is_u ? wu.z : wo.z,
                                     is_u ? wu.w : wo.w));
         }
     }
     if constexpr (MODE == MODE_MERGE) {
-        if (tid == 0) p.nlog[sh * NV + vt] = 0;
+        if (tid == 0) p.nlog[shv] = 0;
     }
     if (!merge) return;
 
@@ -899,22 +1039,30 @@ dl_replay_prep_kernel(const StepParams p) {
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT>
 static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipStream_t s) {
     constexpr int NT = Tile<D, BV, ST>::NT;
-    const dim3 grid(p.nunits), block(NT);
+    constexpr int NV = D / BV;
+    const dim3 block(NT);
+    if (mode == MODE_REPLAY_PREP) {
+        dl_replay_prep_kernel<D, DECAY, DELTA, ST, IT><<<dim3(p.nunits), block, shmem, s>>>(p);
+        return hipGetLastError();
+    }
+    // decode / eager / merge: one grid row per batch entry
+    const int per_entry = p.H_v * NV;
+    if (p.H_k <= 0 || p.H_v % p.H_k != 0 || p.nunits % per_entry != 0) return hipErrorInvalidValue;
+    const dim3 grid(per_entry, p.nunits / per_entry);
+    const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
+    const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
     switch (mode) {
     case MODE_STEP:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     case MODE_EAGER:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     case MODE_MERGE:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     case MODE_STEP_SPLIT:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.nunits, p.H_v, p.H_k, p.C, p);
-        break;
-    case MODE_REPLAY_PREP:
-        dl_replay_prep_kernel<D, DECAY, DELTA, ST, IT><<<grid, block, shmem, s>>>(p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     default:
         return hipErrorInvalidValue;
