@@ -419,20 +419,51 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
 
     // ---- 1. every load of the block is issued before any is consumed: the
     //         token inputs (while the counter is in flight), the whole live
-    //         log, then the base tile.
+    //         log, then the base tile.  In narrow-tile decode launches every
+    //         lane issues the token loads alike (clamped indices, values used
+    //         by the lanes that need them), which keeps the in-order wait
+    //         counts exact: the wait for the snapshots below then lets the
+    //         later loads stay in flight.  Elsewhere only the lanes that use
+    //         them load.
     float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
+    float lp0 = 0.f;                                    // l' (narrow tiles with a scalar decay: every lane)
     IT kraw{};
+    auto token_loads = [&]() {
+        const uint32_t qo = ek * D + (tid % D);
+        qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+        kraw = reinterpret_cast<const IT *>(p.k)[qo];
+        kv = to_f32(kraw);
+        vv = to_f32(reinterpret_cast<const IT *>(p.v)[ev * D + c0 + (tid % BV)]);
+        if constexpr (SCALAR) lam = p.lam[ev];
+        if constexpr (PERKEY) lam = p.lam[ev * D + (tid % D)];
+        if constexpr (DELTA) beta = p.beta[ev];
+    };
     if constexpr (TOKEN) {
-        if (tid < D) {
-            const uint32_t qo = ek * D + tid;
-            qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
-            kraw = reinterpret_cast<const IT *>(p.k)[qo];
-            kv = to_f32(kraw);
-            if (tid < BV) vv = to_f32(reinterpret_cast<const IT *>(p.v)[ev * D + c0 + tid]);
-            if constexpr (SCALAR) lam = p.lam[ev];
-            if constexpr (PERKEY) lam = p.lam[ev * D + tid];
-            if constexpr (DELTA) beta = p.beta[ev];
-        }
+        if constexpr (SMALL) token_loads();
+        else if (tid < D) token_loads();
+    }
+    const IT *klog = reinterpret_cast<const IT *>(p.klog);
+    const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
+    const float *lamlog = p.lamlog;
+    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gkC * D);
+    const BT *ub = ulog + shC * D + c0;
+    const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + shC * D);
+
+    // Narrow tiles: every snapshot (scalar decay) and the first round of key
+    // entries and of value-factor chunks are loaded for the log's whole
+    // capacity while the counter is in flight, and only the live entries are
+    // staged once it has landed: at small batch the stale entries cost no
+    // time, and the log does not wait a round trip behind the counter.  Lane
+    // i of every wave holds snapshot i.  (Decode launches have C >= 1: a pool
+    // with L = 1 decodes with the eager kernel, and the launcher refuses
+    // otherwise.)
+    constexpr int RK = SMALL ? 2 : 1;                   // key rounds loaded up front (longer logs stream)
+    constexpr int RU = SMALL ? 2 : 1;                   // value-factor rounds loaded up front
+    uint4 pk[RK][2], pu[RU];
+    float lam_w = 0.f, pl[RK] = {};                     // snapshots: of lane i's entry i / of the lane's key entry
+    if constexpr (SMALL && SCALAR) {
+        lam_w = lamlog[shC + min(lane, C - 1)];
+        pl[0] = lamlog[shC + min(tid / TPE2, C - 1)];
     }
     // q and a on the keys of this thread's key chunks (the same positions for
     // every chunk it stages), kept packed until used
@@ -448,6 +479,13 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
             apk[c] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const IT *>(p.k) + qo + c * KV);
         }
     }
+    if constexpr (SMALL) {
+        const uint4 *src = kb + (size_t)min(tid / TPE2, C - 1) * CPE + (tid % TPE2) * 2;
+        pk[0][0] = src[0];
+        pk[0][1] = src[1];
+        const int u = min(tid, C * UCH - 1), j = u / UCH;
+        pu[0] = *reinterpret_cast<const uint4 *>(ub + (size_t)j * D + (u - j * UCH) * UV);
+    }
 
     int n = 0;
     if constexpr (HINTED) {
@@ -462,18 +500,16 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     bool merge = !STEP || (n == C);
     const bool fused = !SPLIT || merge;                 // this block replays its own coefficients
 
-    const IT *klog = reinterpret_cast<const IT *>(p.klog);
-    const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
-    const float *lamlog = p.lamlog;
-
-    if constexpr (LOG) {
-        if (tid < D && n > 0) {
-            if constexpr (SCALAR) lbar = lamlog[shC + (n - 1)];
-            if constexpr (PERKEY) lbar = lamlog[(shC + (n - 1)) * D + tid];
+    if constexpr (!(SMALL && SCALAR)) {
+        if constexpr (LOG) {
+            if (tid < D && n > 0) {
+                if constexpr (SCALAR) lbar = lamlog[shC + (n - 1)];
+                if constexpr (PERKEY) lbar = lamlog[(shC + (n - 1)) * D + tid];
+            }
         }
-    }
-    if constexpr (SCALAR && LOG) {
-        if (fused && tid < n) lam_i = lamlog[shC + tid];
+        if constexpr (SCALAR && LOG) {
+            if (fused && tid < n) lam_i = lamlog[shC + tid];
+        }
     }
     // split replay: this append's coefficients from the scratch (c^q, c^k per
     // live entry, then a . q)
@@ -507,9 +543,6 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         s_ll = reinterpret_cast<float *>(s_log + (size_t)(cK + cU) * 16);
     };
     log_layout();
-    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gkC * D);
-    const BT *ub = ulog + shC * D + c0;
-    const uint4 *lb = reinterpret_cast<const uint4 *>(lamlog + shC * D);
     auto chunk_ptr = [&](int x) -> const uint4 * {
         if (x < cK) return kb + x;
         if (x < cK + cU) {
@@ -542,29 +575,37 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     // narrow tiles: round r of key entries (entry r EPR + tid / TPE2, two
     // chunks per lane), staged with their raw dot products; value-factor
     // chunks u = r NT + tid
-    auto k_load = [&](const int r, uint4 (&w)[2]) {
+    // (with a scalar decay, each lane also holds its entry's snapshot and the
+    // coefficients leave weighted by e^{l'-Lam_i}; the weight is kept for a
+    // merge.  The keys reach LDS only for a merge, the one reader of them.)
+    auto k_load = [&](const int r, uint4 (&w)[2], float &le) {
         const int i = r * EPR + tid / TPE2;
         if (i < n) {
             const uint4 *src = kb + (size_t)i * CPE + (tid % TPE2) * 2;
             w[0] = src[0];
             w[1] = src[1];
+            if constexpr (SCALAR) le = lamlog[shC + i];
         }
     };
-    auto k_stage = [&](const int r, const uint4 (&w)[2]) {   // every lane, uniform r (DPP sums)
+    auto k_stage = [&](const int r, const uint4 (&w)[2], const float le) {   // every lane, uniform r (DPP sums)
         const int i = r * EPR + tid / TPE2;
         float pq = 0.f, pk = 0.f;
         if (i < n) {
-            const int x = i * CPE + (tid % TPE2) * 2;
-            stage(x, w[0]);
-            stage(x + 1, w[1]);
+            if (merge) {
+                const int x = i * CPE + (tid % TPE2) * 2;
+                stage(x, w[0]);
+                stage(x + 1, w[1]);
+            }
             pq = dot16<IT>(w[0], qpk[0]) + dot16<IT>(w[1], qpk[QP - 1]);
             if constexpr (DELTA) pk = dot16<IT>(w[0], apk[0]) + dot16<IT>(w[1], apk[QP - 1]);
         }
         pq = group_sum<TPE2>(pq);
         if constexpr (DELTA) pk = group_sum<TPE2>(pk);
         if (i < n && tid % TPE2 == 0) {
-            s_cq[i] = pq;
-            if constexpr (DELTA) s_ck[i] = pk;
+            const float wt = SCALAR ? __expf(lp0 - le) : 1.f;
+            s_cq[i] = pq * wt;
+            if constexpr (DELTA) s_ck[i] = pk * wt;
+            if (merge) s_w[i] = wt;
         }
     };
     auto u_load = [&](const int r, uint4 &w) {
@@ -578,20 +619,17 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         const int u = r * NT + tid;
         if (u < cU) stage(cK + u, w);
     };
-    constexpr int RK = SMALL ? 2 : 1;                   // key rounds loaded up front (longer logs stream)
-    constexpr int RU = SMALL ? 2 : 1;                   // value-factor rounds loaded up front
-    uint4 pk[RK][2], pu[RU];
     // (the chunk rounds past the live log are left by a uniform branch: a
     // short log pays for the rounds it uses, not for the capacity's)
     uint4 pf[PF];
-    if constexpr (SMALL) {
+    if constexpr (SMALL) {                              // round 0 is in flight already
 #pragma unroll
-        for (int r = 0; r < RK; ++r) {
+        for (int r = 1; r < RK; ++r) {
             if (r * EPR >= n) break;
-            k_load(r, pk[r]);
+            k_load(r, pk[r], pl[r]);
         }
 #pragma unroll
-        for (int r = 0; r < RU; ++r) {
+        for (int r = 1; r < RU; ++r) {
             if (r * NT >= cU) break;
             u_load(r, pu[r]);
         }
@@ -631,10 +669,13 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
             if (tid < BV) s_v[tid] = vv;
         }
     };
+    if constexpr (SMALL && SCALAR)                      // snapshot n - 1 from lane n - 1 (uniform n)
+        lbar = n > 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_w), n - 1)) : 0.f;
+    lp0 = lbar + lam;
     if (tid < D) stage_decay(lbar);
     if constexpr (LOG) {
         if constexpr (SCALAR) {
-            if (fused && tid < n) s_lam[tid] = lam_i;
+            if (!SMALL && fused && tid < n) s_lam[tid] = lam_i;
         }
         if constexpr (SPLIT) {
             if (!fused) {
@@ -649,12 +690,13 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
 #pragma unroll
             for (int r = 0; r < RK; ++r) {
                 if (r * EPR >= n) break;
-                k_stage(r, pk[r]);
+                k_stage(r, pk[r], pl[r]);
             }
             for (int r = RK; r * EPR < n; ++r) {        // long logs
                 uint4 w[2];
-                k_load(r, w);
-                k_stage(r, w);
+                float le = 0.f;
+                k_load(r, w, le);
+                k_stage(r, w, le);
             }
 #pragma unroll
             for (int r = 0; r < RU; ++r) {
@@ -708,22 +750,29 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
             n = min(max(nd, 0), C);
             merge = n == C;
             log_layout();
-            if (tid < D) {
-                float lb = 0.f;
-                if (n > 0) {
-                    if constexpr (SCALAR) lb = lamlog[shC + (n - 1)];
-                    if constexpr (PERKEY) lb = lamlog[(shC + (n - 1)) * D + tid];
+            if constexpr (SMALL && SCALAR) {
+                lbar = n > 0 ? lamlog[shC + (n - 1)] : 0.f;
+                lp0 = lbar + lam;
+                if (tid < D) stage_decay(lbar);
+            } else {
+                if (tid < D) {
+                    float lb = 0.f;
+                    if (n > 0) {
+                        if constexpr (SCALAR) lb = lamlog[shC + (n - 1)];
+                        if constexpr (PERKEY) lb = lamlog[(shC + (n - 1)) * D + tid];
+                    }
+                    stage_decay(lb);
                 }
-                stage_decay(lb);
-            }
-            if constexpr (SCALAR) {
-                if (tid < n) s_lam[tid] = lamlog[shC + tid];
+                if constexpr (SCALAR) {
+                    if (tid < n) s_lam[tid] = lamlog[shC + tid];
+                }
             }
             if constexpr (SMALL) {
                 for (int r = 0; r * EPR < n; ++r) {
                     uint4 w[2];
-                    k_load(r, w);
-                    k_stage(r, w);
+                    float le = 0.f;
+                    k_load(r, w, le);
+                    k_stage(r, w, le);
                 }
                 for (int r = 0; r * NT < cU; ++r) {
                     uint4 w;
@@ -770,7 +819,8 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         if constexpr (LOG) {
             for (int i = rg; i < n; i += RG) {             // log entries as extra rows
                 // staged raw dot products carry their decay weight here
-                const float wi = (FC && SCALAR) ? __expf(s_lp[0] - s_lam[i]) : 1.f;
+                // (narrow tiles stage them weighted)
+                const float wi = (FC && SCALAR && !SMALL) ? __expf(s_lp[0] - s_lam[i]) : 1.f;
                 const float cq = s_cq[i] * wi, ck = s_ck[i] * wi;
                 float u[VEC];
                 lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
@@ -919,7 +969,9 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         for (int i = 0; i < n; ++i) {
             float u[VEC];
             lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
-            const float w = PERKEY ? 0.f : (FC ? (SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f) : s_w[i]);
+            const float w = PERKEY ? 0.f
+                          : SMALL ? (SCALAR ? s_w[i] : 1.f)
+                                  : (FC ? (SCALAR ? __expf(s_lp[0] - s_lam[i]) : 1.f) : s_w[i]);
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int r = rg + RG * j;
@@ -1048,6 +1100,7 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     // decode / eager / merge: one grid row per batch entry
     const int per_entry = p.H_v * NV;
     if (p.H_k <= 0 || p.H_v % p.H_k != 0 || p.nunits % per_entry != 0) return hipErrorInvalidValue;
+    if (mode != MODE_EAGER && p.C < 1) return hipErrorInvalidValue;    // the log kernels need a log
     const dim3 grid(per_entry, p.nunits / per_entry);
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
     const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
