@@ -1088,6 +1088,12 @@ dl_replay_prep_kernel(const StepParams p) {
     if (tid == 0) cf[2 * C] = s_s;
 }
 
+}  // namespace dl
+
+#include "dl_small.hpp"
+
+namespace dl {
+
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT>
 static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipStream_t s) {
     constexpr int NT = Tile<D, BV, ST>::NT;
@@ -1104,12 +1110,21 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     const dim3 grid(per_entry, p.nunits / per_entry);
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
     const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
+    // narrow tiles at d = 128 with a scalar or no decay: decode and eager steps
+    // run the one-barrier kernel
+    constexpr bool NARROW = D == 128 && BV <= 32 && DECAY != DECAY_PER_KEY;
     switch (mode) {
     case MODE_STEP:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        if constexpr (NARROW)
+            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, false><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        else
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     case MODE_EAGER:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        if constexpr (NARROW)
+            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, true><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        else
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
         break;
     case MODE_MERGE:
         dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);

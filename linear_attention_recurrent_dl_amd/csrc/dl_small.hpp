@@ -1,0 +1,422 @@
+// Narrow-tile decode and eager kernels: d = 128, value tiles of 16 or 32
+// columns (the library's default at small batch), scalar or no decay.
+//
+// Same arithmetic as dl_step_kernel ([DL] Eq. 3, the append-merge cycle and
+// the GPU-execution section), laid out for launches whose blocks each have a
+// CU to themselves.  There a wave issues about one instruction per four
+// cycles and every barrier is a full stop, so the block is built around one
+// barrier before the output:
+//
+//   - each thread takes q and k on its own tile rows straight from the token
+//     arrays (the decayed q~ and k~ need no LDS round trip), so the tile's
+//     projections start as soon as the tile lands;
+//   - the log is replayed by entries: a lane holds two key chunks of one
+//     entry (TPE2 lanes per entry) and that entry's value factor on UPL
+//     columns of the tile; the entry's replay coefficients (DPP sums over its
+//     lanes, weighted e^{l'-Lam_i}) multiply the value factor in the same
+//     lanes, and the products are summed over the wave's entries with row
+//     swaps, so no coefficient crosses a wave;
+//   - the per-wave tile and log partial sums meet in LDS behind the one
+//     barrier, where the output lanes finish the columns.
+//
+// The live length always comes from the device counter (a scalar load issued
+// with the token loads; the host's value in the slot word is not needed), and
+// the first round of log entries is loaded for the log's whole capacity while
+// the counter is in flight.  Keys, value factors and weights reach LDS only
+// for a merge, which needs them row by row.
+#pragma once
+
+namespace dl {
+
+// UPL consecutive value-factor elements of type T, as fp32 (UPL * sizeof(T) in
+// {2, 4, 8, 16} bytes, naturally aligned).
+template <typename T, int UPL>
+__device__ __forceinline__ void ld_cols(const T *src, float (&x)[UPL]) {
+    constexpr int BYTES = UPL * (int)sizeof(T);
+    if constexpr (sizeof(T) == 4) {
+        if constexpr (UPL == 1) {
+            x[0] = *reinterpret_cast<const float *>(src);
+        } else if constexpr (UPL == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(src);
+            x[0] = v.x;
+            x[1] = v.y;
+        } else {
+            static_assert(UPL == 4, "fp32 columns");
+            const float4 v = *reinterpret_cast<const float4 *>(src);
+            x[0] = v.x;
+            x[1] = v.y;
+            x[2] = v.z;
+            x[3] = v.w;
+        }
+    } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+        if constexpr (BYTES == 2) {
+            w[0] = *reinterpret_cast<const uint16_t *>(src);
+        } else if constexpr (BYTES == 4) {
+            w[0] = *reinterpret_cast<const uint32_t *>(src);
+        } else if constexpr (BYTES == 8) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+            static_assert(BYTES == 16, "bf16 columns");
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            w[0] = v.x;
+            w[1] = v.y;
+            w[2] = v.z;
+            w[3] = v.w;
+        }
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) x[u] = __uint_as_float((u & 1 ? w[u / 2] >> 16 : w[u / 2] & 0xFFFFu) << 16);
+    }
+}
+
+template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, bool EAGER>
+__global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
+dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gmag, const StepParams p) {
+    using G = Tile<D, BV, ST>;
+    using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
+    constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    constexpr int NV = D / BV;
+    constexpr int KV = 16 / (int)sizeof(IT);      // key elements per 16-byte chunk
+    constexpr int CPE = D / KV;                   // key chunks per log entry
+    constexpr int TPE2 = CPE / 2;                 // lanes per log entry (two chunks each)
+    constexpr int EPR = NT / TPE2;                // log entries per round
+    constexpr int UPL = BV / TPE2;                // value-factor columns per lane
+    constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte store
+    constexpr bool SCALAR = DECAY == DECAY_SCALAR;
+    static_assert(DECAY != DECAY_PER_KEY, "scalar or no decay");
+    static_assert(!G::RAGGED && RPT * RG == D, "tile rows");
+    static_assert(UPL >= 1 && UPL * sizeof(BT) <= 16 && BV % UV == 0, "value-factor columns");
+    static_assert(TPE2 >= 2 && TPE2 <= 64 && 64 % TPE2 == 0, "entry lanes within a wave");
+
+    // partial projections per wave: [tile, log][wave][q, k][column], read
+    // back as float4 slots, NQ = BV / 2 per (source, wave)
+    constexpr int NQ = BV / 2;
+    __shared__ __align__(16) float s_part[2][NW][2][BV];
+    __shared__ __align__(16) float s_b[BV];             // b on the tile's columns (merge broadcast)
+    __shared__ float s_w[kMaxLogCap + 1];               // e^{l'-Lam_i} (merge)
+    extern __shared__ float4 s_dyn[];                   // merge: K [n][D] (IT), then U [n][BV] (BT)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ux = xcd_unit(blockIdx.x, H_v * NV);
+    const int e = blockIdx.y;                           // batch entry of this launch
+    const int h = ux / NV, vt = ux - h * NV;            // v-head, value tile
+    const int eh = e * H_v + h;
+    const int c0 = vt * BV;                             // first column of the tile
+    const int g = gmag ? (int)__umulhi((uint32_t)h, gmag) : h;
+    const bool kwriter = h == 0 || gmag == 0 || (int)__umulhi((uint32_t)(h - 1), gmag) != g;
+    const uint32_t sword = p.slots[e];
+    asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
+                 "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(sword));
+    const uint32_t slot = sword & kSlotMask;
+    const uint32_t sh32 = slot * (uint32_t)H_v + (uint32_t)h;
+    const uint32_t gk32 = slot * (uint32_t)H_k + (uint32_t)g;
+    const uint32_t shv = sh32 * NV + (uint32_t)vt;      // (slot-head, value tile)
+    const size_t shC = (size_t)sh32 * (uint32_t)C;      // the slot-head's first log entry
+    const size_t gkC = (size_t)gk32 * (uint32_t)C;      // the q/k head's first key-log entry
+    const uint32_t ek = (uint32_t)e * H_k + g;          // token row of q, k
+    const uint32_t ev = (uint32_t)eh;                   // token row of v, lambda, beta, output
+    // tile geometry: the LPG lanes of a column group sit in one aligned run of
+    // a wave, so their partial sums close with DPP moves inside a row
+    constexpr int LPG = 64 / CG;
+    const int cg = lane / LPG, rg = wave * LPG + lane % LPG;
+    const int jk = tid % TPE2;                          // the lane's place within its log entry
+    const bool owner = vt == 0;                         // writes the tile-shared log metadata
+
+    // output and appended value factor: NO lanes cover 4 output columns each,
+    // then NU lanes one value-factor chunk (UV columns) each
+    constexpr int NO = BV / 4;
+    constexpr int NU = EAGER ? 0 : BV / UV;
+    constexpr int MC = UV > 4 ? UV : 4;
+    static_assert(NO + NU <= 64, "column lanes fit one wave");
+    const bool is_u = tid >= NO;
+    const int cb = is_u ? min(tid - NO, (NU > 0 ? NU : 1) - 1) * UV : tid * 4;   // first column (clamped)
+    const int nc = is_u ? UV : 4;
+
+    // ---- loads, all issued before any is consumed (v of the lane's output
+    // columns too: a load only the output lanes consume would be sunk behind
+    // the others)
+    int n_dev = 0;
+    if constexpr (!EAGER) n_dev = ((const __attribute__((address_space(4))) int32_t *)(size_t)p.nlog)[shv];
+    const IT *qg = reinterpret_cast<const IT *>(p.q) + ek * D;
+    const IT *kg = reinterpret_cast<const IT *>(p.k) + ek * D;
+    float qr[RPT], kr[RPT];                             // q and a (= k) on the thread's tile rows
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        qr[j] = to_f32(qg[rg + RG * j]);
+        kr[j] = to_f32(kg[rg + RG * j]);
+    }
+    float vc[MC];
+    {
+        const IT *vg = reinterpret_cast<const IT *>(p.v) + ev * D + c0 + cb;
+#pragma unroll
+        for (int c = 0; c < MC; ++c) vc[c] = to_f32(vg[c < nc ? c : 0]);
+    }
+    float lam = 0.f, beta = 0.f;
+    if constexpr (SCALAR) lam = p.lam[ev];
+    if constexpr (DELTA) beta = p.beta[ev];
+    uint4 qc[2], ac[2];                                 // q and a on the lane's two key chunks
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        qc[c] = *reinterpret_cast<const uint4 *>(qg + (jk * 2 + c) * KV);
+        ac[c] = *reinterpret_cast<const uint4 *>(kg + (jk * 2 + c) * KV);
+    }
+    const IT *klog = reinterpret_cast<const IT *>(p.klog);
+    const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
+    const float *lamlog = p.lamlog;
+    const uint4 *kb = reinterpret_cast<const uint4 *>(klog + gkC * D);
+    const BT *ub = ulog + shC * D + c0;
+    // round 0 of the log for the whole capacity (C >= 1 in a decode launch):
+    // entry i0 = tid / TPE2 (clamped), its snapshot, its value factor on the
+    // lane's columns; lane i of every wave also holds snapshot i
+    float lam_w = 0.f, le0 = 0.f, uu0[UPL];
+    uint4 kc0[2];
+    if constexpr (!EAGER) {
+        const int i0 = min(tid / TPE2, C - 1);
+        if constexpr (SCALAR) {
+            lam_w = lamlog[shC + min(lane, C - 1)];
+            le0 = lamlog[shC + i0];
+        }
+        const uint4 *src = kb + (size_t)i0 * CPE + jk * 2;
+        kc0[0] = src[0];
+        kc0[1] = src[1];
+        ld_cols<BT, UPL>(ub + (size_t)i0 * D + jk * UPL, uu0);
+    }
+    const ST *tbase = reinterpret_cast<const ST *>(p.base) + (size_t)shv * (D * BV);
+    const uint32_t toff = (uint32_t)((rg * BV + cg * VEC) * sizeof(ST));
+    constexpr uint32_t TROW = RG * BV * sizeof(ST);     // bytes between a thread's rows
+    uint4 tile[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) tile[j] = ld16(tbase, toff + j * TROW);
+
+    // ---- live length, l' = l_bar + lambda
+    int n = 0;
+    if constexpr (!EAGER) n = min(max(__builtin_amdgcn_readfirstlane(n_dev), 0), C);
+    const bool merge = EAGER || n == C;
+    float lbar = 0.f;
+    if constexpr (SCALAR && !EAGER) {                   // newest snapshot, from lane n - 1 (uniform n)
+        // (read unconditionally: a read inside a branch on n lets the compiler
+        // sink the snapshot load behind every other load)
+        const float lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_w), max(n - 1, 0)));
+        lbar = n > 0 ? lw : 0.f;
+    }
+    const float lp = lbar + lam;
+    const float gg = SCALAR ? __expf(lp) : 1.f;         // e^{l'}
+
+    // ---- log replay by entries (decode)
+    char *s_log = reinterpret_cast<char *>(s_dyn);
+    const IT *s_lk = reinterpret_cast<const IT *>(s_log);
+    BT *s_lu = reinterpret_cast<BT *>(s_log + (size_t)C * CPE * 16);
+    if constexpr (!EAGER) {
+        float lq[UPL], lk[UPL];
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) lq[u] = lk[u] = 0.f;
+        // one round: every lane of the block, uniform r (DPP sums)
+        auto replay_round = [&](const int r, const uint4 (&kc)[2], const float le, const float (&uu)[UPL]) {
+            const int i = r * EPR + tid / TPE2;
+            float pq = dot16<IT>(kc[0], qc[0]) + dot16<IT>(kc[1], qc[1]);
+            float pk = 0.f;
+            if constexpr (DELTA) pk = dot16<IT>(kc[0], ac[0]) + dot16<IT>(kc[1], ac[1]);
+            pq = group_sum<TPE2>(pq);
+            if constexpr (DELTA) pk = group_sum<TPE2>(pk);
+            // (computed in every lane, zero past the live log: a snapshot or
+            // value factor used only under a branch would have its load sunk
+            // behind all the others)
+            const bool live = i < n;
+            const float w = SCALAR ? __expf(lp - le) : 1.f;
+            const float cq = live ? pq * w : 0.f, ck = live ? pk * w : 0.f;
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                lq[u] += cq * uu[u];
+                if constexpr (DELTA) lk[u] += ck * uu[u];
+            }
+            if (live) {
+                if (merge) {
+                    uint4 *dk = reinterpret_cast<uint4 *>(s_log) + (size_t)i * CPE + jk * 2;
+                    dk[0] = make_uint4(kc[0].x, kc[0].y, kc[0].z, kc[0].w);
+                    dk[1] = make_uint4(kc[1].x, kc[1].y, kc[1].z, kc[1].w);
+#pragma unroll
+                    for (int u = 0; u < UPL; ++u) s_lu[i * BV + jk * UPL + u] = from_f32<BT>(uu[u]);
+                    if (jk == 0) s_w[i] = w;
+                }
+            }
+        };
+        replay_round(0, kc0, le0, uu0);
+        for (int r = 1; r * EPR < n; ++r) {             // logs longer than one round
+            const int i = r * EPR + tid / TPE2;
+            uint4 kc[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+            float le = 0.f, uu[UPL];
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) uu[u] = 0.f;
+            if (i < n) {
+                const uint4 *src = kb + (size_t)i * CPE + jk * 2;
+                kc[0] = src[0];
+                kc[1] = src[1];
+                if constexpr (SCALAR) le = lamlog[shC + i];
+                ld_cols<BT, UPL>(ub + (size_t)i * D + jk * UPL, uu);
+            }
+            replay_round(r, kc, le, uu);
+        }
+        // sum over the wave's entries: lanes that agree modulo TPE2 hold the same columns
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) {
+            lq[u] = strided_sum<TPE2>(lq[u]);
+            if constexpr (DELTA) lk[u] = strided_sum<TPE2>(lk[u]);
+        }
+        if (lane < TPE2) {
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                s_part[1][wave][0][jk * UPL + u] = lq[u];
+                s_part[1][wave][1][jk * UPL + u] = lk[u];
+            }
+        }
+    }
+
+    // ---- tile projections: y~ = S_bar^T q~, S_bar^T k~ over the thread's rows
+    float accq[VEC], acck[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) accq[c] = acck[c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        float x[VEC];
+        unpack_f32<ST, VEC>(tile[j], x);
+        const float qd = gg * qr[j], kd = gg * kr[j];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            accq[c] += x[c] * qd;
+            if constexpr (DELTA) acck[c] += x[c] * kd;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+        accq[c] = group_sum<LPG>(accq[c]);
+        if constexpr (DELTA) acck[c] = group_sum<LPG>(acck[c]);
+    }
+    if (lane % LPG == 0) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+            s_part[0][wave][0][cg * VEC + c] = accq[c];
+            s_part[0][wave][1][cg * VEC + c] = acck[c];
+        }
+    }
+    // a . q, from the first entry's lanes, in lanes 0-15 (the column lanes)
+    float aq = 0.f;
+    if (tid < TPE2) aq = dot16<IT>(qc[0], ac[0]) + dot16<IT>(qc[1], ac[1]);
+    aq = group_sum<16>(aq);
+    // stores that need no reduced value: the appended key (first v-head of
+    // the q/k group, first tile) and decay snapshot, the live-length counter
+    if constexpr (!EAGER) {
+        if (!merge && owner) {
+            if (kwriter && tid < TPE2) {
+                uint4 *dk = reinterpret_cast<uint4 *>(reinterpret_cast<IT *>(p.klog) + (gkC + n) * D) + jk * 2;
+                dk[0] = ac[0];
+                dk[1] = ac[1];
+            }
+            if constexpr (SCALAR) {
+                if (tid == 0) p.lamlog[shC + n] = lp;
+            }
+        }
+        if (tid == 0) p.nlog[shv] = merge ? 0 : n + 1;
+    }
+    __syncthreads();
+
+    // ---- output and appended value factor (wave 0).  Each lane reads float4
+    // slot(s) of the partial sums; lanes that agree modulo NQ hold the same
+    // (q or k, 4 columns), whose sources and waves the row swaps then add:
+    // lane j < BV/4 ends with y~_q on columns 4j.., lane BV/4 + j with y~_k.
+    if (wave != 0) {
+        if (!merge) return;
+    } else {
+    constexpr int SPL = 2 * NW * NQ / 64;              // slots per lane
+    static_assert(SPL * 64 == 2 * NW * NQ && 64 % NQ == 0, "partial-sum slots");
+    const float4 *slots = reinterpret_cast<const float4 *>(&s_part[0][0][0][0]);
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+        const int idx = lane + 64 * s;
+        if (!EAGER || idx < NW * NQ) {                  // (eager: no log half)
+            const float4 a = slots[idx];
+            r[0] += a.x; r[1] += a.y; r[2] += a.z; r[3] += a.w;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = strided_sum<NQ>(r[c]);
+    // y~_k of an output lane's columns sits BV/4 lanes up, in the same row
+    // (moved while every lane of the wave is active: DPP reads no lane that
+    // EXEC disables)
+    float yka[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(r[c]), 0x100 + BV / 4,
+                                                                   0xf, 0xf, false));
+        yka[c] = is_u ? r[c] : up;
+    }
+    if (tid < NO || (tid < NO + NU && !merge)) {
+        float ov[MC], bc[MC];
+#pragma unroll
+        for (int c4 = 0; c4 < MC; c4 += 4) {
+            if (c4 < nc) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float b = DELTA ? beta * (vc[c4 + j] - yka[j]) : vc[c4 + j];
+                    bc[c4 + j] = b;
+                    ov[c4 + j] = r[j] + aq * b;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bc[c4 + j] = ov[c4 + j] = 0.f;
+            }
+        }
+        if (merge && !is_u) *reinterpret_cast<float4 *>(&s_b[cb]) = make_float4(bc[0], bc[1], bc[2], bc[3]);
+        const uint4 wo = make_uint4(__float_as_uint(ov[0]), __float_as_uint(ov[1]), __float_as_uint(ov[2]),
+                                    __float_as_uint(ov[3]));
+        uint4 wu = wo;
+        if constexpr (!EAGER) {
+            float ub4[UV];
+#pragma unroll
+            for (int c = 0; c < UV; ++c) ub4[c] = bc[c];
+            wu = pack_16<BT, UV>(ub4);
+        }
+        char *dst = is_u ? reinterpret_cast<char *>(p.ulog) + ((shC + n) * D + c0 + cb) * sizeof(BT)
+                         : reinterpret_cast<char *>(p.out) + ((size_t)ev * D + c0 + cb) * sizeof(float);
+        // per-component select: a select of whole vectors goes through scratch
+        st16_stream(dst, 0, make_uint4(is_u ? wu.x : wo.x, is_u ? wu.y : wo.y, is_u ? wu.z : wo.z,
+                                       is_u ? wu.w : wo.w));
+    }
+    if (!merge) return;
+    }
+
+    // ---- merge (eager: every step): S_bar <- e^{l'} S_bar + sum_i (e^{l'-Lam_i} K_i) U_i^T + a b^T,
+    // from the tile still in registers
+    __syncthreads();
+    float bcol[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) bcol[c] = s_b[cg * VEC + c];
+    float acc[RPT][VEC];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        unpack_f32<ST, VEC>(tile[j], acc[j]);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[j][c] = gg * acc[j][c] + kr[j] * bcol[c];
+    }
+    if constexpr (!EAGER) {
+        for (int i = 0; i < n; ++i) {
+            float u[VEC];
+            lds_f32<BT, VEC>(s_lu + i * BV + cg * VEC, u);
+            const float w = s_w[i];
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const float kt = to_f32(s_lk[i * D + rg + RG * j]) * w;
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) acc[j][c] += kt * u[c];
+            }
+        }
+    }
+    ST *basew = const_cast<ST *>(tbase);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) st16(basew, toff + j * TROW, pack_16<ST, VEC>(acc[j]));
+}
+
+}  // namespace dl
