@@ -138,8 +138,24 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     // ---- loads, all issued before any is consumed (v of the lane's output
     // columns too: a load only the output lanes consume would be sunk behind
     // the others)
+    // the counter and the per-head scalars go out first, through the scalar
+    // path (their round trip then overlaps the vector loads' issue; the
+    // scheduling barrier keeps the compiler from moving them behind)
+    typedef const __attribute__((address_space(4))) int32_t *cint_p;
+    typedef const __attribute__((address_space(4))) float *cfloat_p;
+    // (the eager kernel, with no counter to wait for, measured faster with
+    // vector loads of the scalars)
     int n_dev = 0;
-    if constexpr (!EAGER) n_dev = ((const __attribute__((address_space(4))) int32_t *)(size_t)p.nlog)[shv];
+    float lam = 0.f, beta = 0.f;
+    if constexpr (!EAGER) {
+        n_dev = ((cint_p)(size_t)p.nlog)[shv];
+        if constexpr (SCALAR) lam = ((cfloat_p)(size_t)p.lam)[ev];
+        if constexpr (DELTA) beta = ((cfloat_p)(size_t)p.beta)[ev];
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        if constexpr (SCALAR) lam = p.lam[ev];
+        if constexpr (DELTA) beta = p.beta[ev];
+    }
     const IT *qg = reinterpret_cast<const IT *>(p.q) + ek * D;
     const IT *kg = reinterpret_cast<const IT *>(p.k) + ek * D;
     float qr[RPT], kr[RPT];                             // q and a (= k) on the thread's tile rows
@@ -151,12 +167,13 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     float vc[MC];
     {
         const IT *vg = reinterpret_cast<const IT *>(p.v) + ev * D + c0 + cb;
+        if constexpr (MC == 4) {
+            ld_cols<IT, 4>(vg, vc);                     // one 16- or 8-byte load
+        } else {
 #pragma unroll
-        for (int c = 0; c < MC; ++c) vc[c] = to_f32(vg[c < nc ? c : 0]);
+            for (int c = 0; c < MC; ++c) vc[c] = to_f32(vg[c < nc ? c : 0]);
+        }
     }
-    float lam = 0.f, beta = 0.f;
-    if constexpr (SCALAR) lam = p.lam[ev];
-    if constexpr (DELTA) beta = p.beta[ev];
     uint4 qc[2], ac[2];                                 // q and a on the lane's two key chunks
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
