@@ -226,12 +226,25 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     char *s_log = reinterpret_cast<char *>(s_dyn);
     const IT *s_lk = reinterpret_cast<const IT *>(s_log);
     BT *s_lu = reinterpret_cast<BT *>(s_log + (size_t)C * CPE * 16);
+    // a live entry's key chunks, value factors and weight into LDS (merge)
+    auto stage_entry = [&](const int i, const uint4 (&kc)[2], const float (&uu)[UPL], const float w) {
+        uint4 *dk = reinterpret_cast<uint4 *>(s_log) + (size_t)i * CPE + jk * 2;
+        dk[0] = make_uint4(kc[0].x, kc[0].y, kc[0].z, kc[0].w);
+        dk[1] = make_uint4(kc[1].x, kc[1].y, kc[1].z, kc[1].w);
+#pragma unroll
+        for (int u = 0; u < UPL; ++u) s_lu[i * BV + jk * UPL + u] = from_f32<BT>(uu[u]);
+        if (jk == 0) s_w[i] = w;
+    };
+    float w0 = 1.f;                                     // weight of the lane's round-0 entry
     if constexpr (!EAGER) {
         float lq[UPL], lk[UPL];
 #pragma unroll
         for (int u = 0; u < UPL; ++u) lq[u] = lk[u] = 0.f;
         // one round: every lane of the block, uniform r (DPP sums)
-        auto replay_round = [&](const int r, const uint4 (&kc)[2], const float le, const float (&uu)[UPL]) {
+        // one round, returning the entry's weight: every lane of the block,
+        // uniform r (DPP sums), no branch (so that the compiler can interleave
+        // it with the tile's projections)
+        auto replay_round = [&](const int r, const uint4 (&kc)[2], const float le, const float (&uu)[UPL]) -> float {
             const int i = r * EPR + tid / TPE2;
             float pq = dot16<IT>(kc[0], qc[0]) + dot16<IT>(kc[1], qc[1]);
             float pk = 0.f;
@@ -249,18 +262,9 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
                 lq[u] += cq * uu[u];
                 if constexpr (DELTA) lk[u] += ck * uu[u];
             }
-            if (live) {
-                if (merge) {
-                    uint4 *dk = reinterpret_cast<uint4 *>(s_log) + (size_t)i * CPE + jk * 2;
-                    dk[0] = make_uint4(kc[0].x, kc[0].y, kc[0].z, kc[0].w);
-                    dk[1] = make_uint4(kc[1].x, kc[1].y, kc[1].z, kc[1].w);
-#pragma unroll
-                    for (int u = 0; u < UPL; ++u) s_lu[i * BV + jk * UPL + u] = from_f32<BT>(uu[u]);
-                    if (jk == 0) s_w[i] = w;
-                }
-            }
+            return w;
         };
-        replay_round(0, kc0, le0, uu0);
+        w0 = replay_round(0, kc0, le0, uu0);
         for (int r = 1; r * EPR < n; ++r) {             // logs longer than one round
             const int i = r * EPR + tid / TPE2;
             uint4 kc[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
@@ -274,7 +278,8 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
                 if constexpr (SCALAR) le = lamlog[shC + i];
                 ld_cols<BT, UPL>(ub + (size_t)i * D + jk * UPL, uu);
             }
-            replay_round(r, kc, le, uu);
+            const float w = replay_round(r, kc, le, uu);
+            if (merge && i < n) stage_entry(i, kc, uu, w);
         }
         // sum over the wave's entries: lanes that agree modulo TPE2 hold the same columns
 #pragma unroll
@@ -406,7 +411,11 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     }
 
     // ---- merge (eager: every step): S_bar <- e^{l'} S_bar + sum_i (e^{l'-Lam_i} K_i) U_i^T + a b^T,
-    // from the tile still in registers
+    // from the tile still in registers; the first round of live entries is
+    // staged here, from registers (later rounds were staged as they came)
+    if constexpr (!EAGER) {
+        if (tid / TPE2 < n) stage_entry(tid / TPE2, kc0, uu0, w0);
+    }
     __syncthreads();
     float bcol[VEC];
 #pragma unroll
