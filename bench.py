@@ -677,6 +677,15 @@ def stream_ceiling(torch, blocks: int, threads: int, bytes_per_launch: float, ro
             "us": us, "GBps": total / (us * 1e-6) / 1e9}
 
 
+def decode_kernel(cfg, value_tile: int) -> str:
+    """Name of the kernel a decode step of the workload runs: the one-barrier
+    narrow-tile kernel at d = 128 with 16- or 32-column tiles and a scalar or
+    no decay, the general kernel otherwise."""
+    if cfg.d == 128 and value_tile <= 32 and cfg.decay != "per_key":
+        return "dl_small_kernel"
+    return "dl_step_kernel"
+
+
 def decode_grid(cfg, value_tile: int):
     """(blocks, threads) of one decode launch of the workload."""
     threads = 256 if cfg.d >= 128 else (128 if cfg.d >= 64 else 64)
@@ -991,7 +1000,7 @@ def make_line(cfg, rotate, steps, warmup, steps_requested, head, eager_head, ext
         "roofline": {"bound": "hbm", "achieved": _r(head["decode_GBps"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": _r(head["decode_GBps"] / PEAK_HBM_GBS, 4),
                      "traffic": traffic_val, "traffic_source": traffic_src,
-                     "kernel": "dl_step_kernel (decode, append/merge)",
+                     "kernel": decode_kernel(cfg, head["value_tile"]) + " (decode, append/merge)",
                      "bytes_per_launch": _r(head["decode_bytes_per_launch"], 1),
                      "launch_us": _r(head["decode_launch_us"], 3),
                      "launch_source": head["decode_launch_source"],

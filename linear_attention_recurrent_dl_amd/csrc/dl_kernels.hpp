@@ -1110,9 +1110,14 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     const dim3 grid(per_entry, p.nunits / per_entry);
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
     const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
-    // narrow tiles at d = 128 with a scalar or no decay: decode and eager steps
-    // run the one-barrier kernel
-    constexpr bool NARROW = D == 128 && BV <= 32 && DECAY != DECAY_PER_KEY;
+    // narrow tiles with a scalar or no decay: decode and eager steps run the
+    // one-barrier kernel where its lane layout fits (at least 4 key chunks per
+    // entry, every thread owning tile rows, at most 32 bytes of value factor
+    // per lane)
+    using BTn = typename std::conditional<DELTA, float, IT>::type;
+    constexpr int CPEn = D / (16 / (int)sizeof(IT));
+    constexpr bool NARROW = BV <= 32 && DECAY != DECAY_PER_KEY && CPEn >= 4 && !Tile<D, BV, ST>::RAGGED &&
+                            (BV / (CPEn / 2)) * (int)sizeof(BTn) <= 32;
     switch (mode) {
     case MODE_STEP:
         if constexpr (NARROW)

@@ -1,5 +1,5 @@
-// Narrow-tile decode and eager kernels: d = 128, value tiles of 16 or 32
-// columns (the library's default at small batch), scalar or no decay.
+// Narrow-tile decode and eager kernels: value tiles of 16 or 32 columns (the
+// library's default at small batch), scalar or no decay.
 //
 // Same arithmetic as dl_step_kernel ([DL] Eq. 3, the append-merge cycle and
 // the GPU-execution section), laid out for launches whose blocks each have a
@@ -29,7 +29,7 @@
 namespace dl {
 
 // UPL consecutive value-factor elements of type T, as fp32 (UPL * sizeof(T) in
-// {2, 4, 8, 16} bytes, naturally aligned).
+// {2, 4, 8, 16, 32} bytes, aligned to the smaller of that and 16).
 template <typename T, int UPL>
 __device__ __forceinline__ void ld_cols(const T *src, float (&x)[UPL]) {
     constexpr int BYTES = UPL * (int)sizeof(T);
@@ -41,15 +41,19 @@ __device__ __forceinline__ void ld_cols(const T *src, float (&x)[UPL]) {
             x[0] = v.x;
             x[1] = v.y;
         } else {
-            static_assert(UPL == 4, "fp32 columns");
-            const float4 v = *reinterpret_cast<const float4 *>(src);
-            x[0] = v.x;
-            x[1] = v.y;
-            x[2] = v.z;
-            x[3] = v.w;
+            static_assert(UPL % 4 == 0 && UPL <= 8, "fp32 columns");
+#pragma unroll
+            for (int c = 0; c < UPL; c += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(src + c);
+                x[c] = v.x;
+                x[c + 1] = v.y;
+                x[c + 2] = v.z;
+                x[c + 3] = v.w;
+            }
         }
     } else {
-        uint32_t w[4] = {0, 0, 0, 0};
+        constexpr int NWD = BYTES >= 4 ? BYTES / 4 : 1;
+        uint32_t w[NWD];
         if constexpr (BYTES == 2) {
             w[0] = *reinterpret_cast<const uint16_t *>(src);
         } else if constexpr (BYTES == 4) {
@@ -59,12 +63,15 @@ __device__ __forceinline__ void ld_cols(const T *src, float (&x)[UPL]) {
             w[0] = v.x;
             w[1] = v.y;
         } else {
-            static_assert(BYTES == 16, "bf16 columns");
-            const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            w[0] = v.x;
-            w[1] = v.y;
-            w[2] = v.z;
-            w[3] = v.w;
+            static_assert(BYTES % 16 == 0 && BYTES <= 32, "bf16 columns");
+#pragma unroll
+            for (int c = 0; c < BYTES / 16; ++c) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(src + 8 * c);
+                w[4 * c] = v.x;
+                w[4 * c + 1] = v.y;
+                w[4 * c + 2] = v.z;
+                w[4 * c + 3] = v.w;
+            }
         }
 #pragma unroll
         for (int u = 0; u < UPL; ++u) x[u] = __uint_as_float((u & 1 ? w[u / 2] >> 16 : w[u / 2] & 0xFFFFu) << 16);
@@ -87,7 +94,7 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
     static_assert(DECAY != DECAY_PER_KEY, "scalar or no decay");
     static_assert(!G::RAGGED && RPT * RG == D, "tile rows");
-    static_assert(UPL >= 1 && UPL * sizeof(BT) <= 16 && BV % UV == 0, "value-factor columns");
+    static_assert(UPL >= 1 && UPL * sizeof(BT) <= 32 && BV % UV == 0, "value-factor columns");
     static_assert(TPE2 >= 2 && TPE2 <= 64 && 64 % TPE2 == 0, "entry lanes within a wave");
 
     // partial projections per wave: [tile, log][wave][q, k][column], read
@@ -254,13 +261,19 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
             // (computed in every lane, zero past the live log: a snapshot or
             // value factor used only under a branch would have its load sunk
             // behind all the others)
+            // Entries past the live log may hold anything (memory never
+            // written yet), so their products are selected away, not scaled by 0.
             const bool live = i < n;
             const float w = SCALAR ? __expf(lp - le) : 1.f;
-            const float cq = live ? pq * w : 0.f, ck = live ? pk * w : 0.f;
+            const float cq = pq * w, ck = pk * w;
 #pragma unroll
             for (int u = 0; u < UPL; ++u) {
-                lq[u] += cq * uu[u];
-                if constexpr (DELTA) lk[u] += ck * uu[u];
+                const float tq = cq * uu[u];
+                lq[u] += live ? tq : 0.f;
+                if constexpr (DELTA) {
+                    const float tk = ck * uu[u];
+                    lk[u] += live ? tk : 0.f;
+                }
             }
             return w;
         };
@@ -351,14 +364,15 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     if (wave != 0) {
         if (!merge) return;
     } else {
-    constexpr int SPL = 2 * NW * NQ / 64;              // slots per lane
-    static_assert(SPL * 64 == 2 * NW * NQ && 64 % NQ == 0, "partial-sum slots");
+    constexpr int NSL = 2 * NW * NQ;                   // slots
+    constexpr int SPL = (NSL + 63) / 64;               // slots per lane
+    static_assert(64 % NQ == 0, "partial-sum slots");
     const float4 *slots = reinterpret_cast<const float4 *>(&s_part[0][0][0][0]);
     float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
         const int idx = lane + 64 * s;
-        if (!EAGER || idx < NW * NQ) {                  // (eager: no log half)
+        if (idx < (EAGER ? NW * NQ : NSL)) {            // (eager: no log half)
             const float4 a = slots[idx];
             r[0] += a.x; r[1] += a.y; r[2] += a.z; r[3] += a.w;
         }

@@ -106,6 +106,17 @@ def test_decode_grid_matches_the_launch():
     assert bench.decode_grid(CONFIGS[1], 16) == (2, 64)
 
 
+def test_decode_kernel_names_the_launched_kernel():
+    from workloads import CONFIGS
+    # the launcher's rule: d = 128, 16- or 32-column tiles, scalar or no decay
+    assert bench.decode_kernel(CONFIGS[2], 16) == "dl_small_kernel"
+    assert bench.decode_kernel(CONFIGS[2], 32) == "dl_small_kernel"
+    assert bench.decode_kernel(CONFIGS[2], 64) == "dl_step_kernel"
+    assert bench.decode_kernel(CONFIGS[4], 16) == "dl_step_kernel"      # per-key decay
+    assert bench.decode_kernel(CONFIGS[1], 16) == "dl_step_kernel"      # d = 16
+    assert bench.decode_kernel(CONFIGS[5], 128) == "dl_step_kernel"
+
+
 def test_line_dtype_names_the_storage_of_16_bit_workloads():
     from workloads import CONFIGS
     assert bench.line_dtype(CONFIGS[2]) == "f32"

@@ -96,3 +96,51 @@ def test_edge_inputs(idx, case):
     assert err.value <= 1e-4 and st_e.value <= 1e-4, (err.value, st_e.value)
     if retrieval:
         assert max(retrieval) <= 1e-4
+
+
+@pytest.mark.parametrize("d,tile,in_dtype,idx", [(128, 16, "f32", 2), (128, 32, "bf16", 2), (32, 32, "bf16", 1),
+                                                 (16, 16, "f32", 1), (64, 32, "f32", 2), (128, 128, "f32", 2)])
+def test_unwritten_log_memory_stays_out_of_outputs(d, tile, in_dtype, idx):
+    """Kernels may load log entries past the live length (a whole round of the
+    capacity, at small batch); whatever that memory holds must not reach the
+    outputs.  The log buffers start as all-ones bytes (NaN in fp32 and bf16),
+    so an entry past the live length that leaks into a sum poisons it."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev, tolerance
+    from oracle import EagerPool, RelL2
+
+    base = CONFIGS[idx]
+    cfg = small_variant(base, batch=2, num_slots=2, steps=24, L=6, d=d, H_v=4, H_k=2 if base.H_k < base.H_v else 4,
+                        in_dtype=in_dtype, name=f"stale_log_{base.name}_d{d}")
+    wl = Workload(cfg)
+    P, Hv, D = cfg.num_slots, cfg.H_v, cfg.d
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    pool = dl.DeltaLogPool(P, Hv, cfg.H_k, D, cfg.L, cfg.decay, cfg.update, cfg.state_dtype, cfg.in_dtype,
+                           max_batch=P, value_tile=tile)
+    for name in ("klog", "ulog", "lamlog"):
+        pool.bufs[name].fill_(0xFF)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, Hv, D, D, cfg.decay, cfg.update, init=wl.init_base(ids))
+    say(f"[gpu] unwritten log memory = NaN bytes: {cfg.describe()} value_tile={pool.value_tile}")
+    err = RelL2()
+    finite = True
+    for d_ in wl.main_steps()[:14]:
+        inp = wl.step_inputs(d_)
+        q, k, v, lam, beta = inp.q, inp.k, inp.v, inp.lam, inp.beta
+        out = pool.decode_step(ids, to_dev(q, it), to_dev(k, it), to_dev(v, it), to_dev(lam, torch.float32),
+                               to_dev(beta, torch.float32)).cpu().numpy()
+        finite &= bool(np.all(np.isfinite(out)))
+        _, o_ref = E.step(ids, q, k, v, lam, beta)
+        err.add(out, o_ref)
+    pool.flush_all()
+    S = pool.read_base(ids).float().cpu().numpy()
+    st_e = RelL2()
+    st_e.add(S, E.states())
+    say(f"[gpu]   out rel-L2 {err.value:.3e}; state rel-L2 {st_e.value:.3e}; outputs finite: {finite}")
+    pool.close()
+    tol = tolerance(cfg)
+    assert finite and np.all(np.isfinite(S))
+    assert err.value <= tol and st_e.value <= tol, (err.value, st_e.value)
