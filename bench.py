@@ -678,10 +678,20 @@ def stream_ceiling(torch, blocks: int, threads: int, bytes_per_launch: float, ro
 
 
 def decode_kernel(cfg, value_tile: int) -> str:
-    """Name of the kernel a decode step of the workload runs: the one-barrier
-    narrow-tile kernel at d = 128 with 16- or 32-column tiles and a scalar or
-    no decay, the general kernel otherwise."""
-    if cfg.d == 128 and value_tile <= 32 and cfg.decay != "per_key":
+    """Name of the kernel a decode step of the workload runs: the launcher's
+    rule for the one-barrier narrow-tile kernel (tiles of at most 32 columns,
+    scalar or no decay, at least four 16-byte key chunks per log entry, every
+    row group owning a tile row, at most 32 bytes of value-side factor per
+    lane), the general kernel otherwise."""
+    isz = 2 if cfg.in_dtype == "bf16" else 4
+    ssz = 2 if cfg.state_dtype == "bf16" else 4
+    bsz = 4 if cfg.update == "delta" else isz            # b is kept in fp32 for the delta rule
+    cpe = cfg.d // (16 // isz)                           # 16-byte chunks per key
+    threads = 256 if cfg.d >= 128 else (128 if cfg.d >= 64 else 64)
+    col_groups = max(1, value_tile // (16 // ssz))
+    ragged = threads // col_groups > cfg.d
+    if (value_tile <= 32 and cfg.decay != "per_key" and cpe >= 4 and not ragged
+            and (value_tile // (cpe // 2)) * bsz <= 32):
         return "dl_small_kernel"
     return "dl_step_kernel"
 

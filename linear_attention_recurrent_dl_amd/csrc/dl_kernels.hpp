@@ -370,7 +370,8 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     // instruction per four cycles, and a division by a run-time value costs
     // about 25 of them ahead of the first load.  The q/k head of v-head h is
     // h / (H_v / H_k), taken as the high word of h * gmag with
-    // gmag = ceil(2^32 / (H_v / H_k)) (exact for h < 2^16), or h when gmag = 0
+    // gmag = ceil(2^32 / (H_v / H_k)) (exact for H_v <= 2^16: the error term
+    // h * (gmag * (H_v / H_k) - 2^32) stays below 2^32), or h when gmag = 0
     // (one v-head per q/k head).
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1109,6 +1110,7 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     if (mode != MODE_EAGER && p.C < 1) return hipErrorInvalidValue;    // the log kernels need a log
     const dim3 grid(per_entry, p.nunits / per_entry);
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
+    if (grp > 1 && p.H_v > 65536) return hipErrorInvalidValue;         // gmag exact below
     const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
     // narrow tiles with a scalar or no decay: decode and eager steps run the
     // one-barrier kernel where its lane layout fits (at least 4 key chunks per

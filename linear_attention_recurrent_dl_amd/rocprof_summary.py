@@ -142,13 +142,15 @@ def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int, last
     dispatches (the timed steps, after set-up and warm-up launches)."""
 
     def rows_of(path, counter):
+        # (name, dispatches in the run, dispatches averaged, average)
         if not last:
-            return pmc_rows(path, counter)
-        per = defaultdict(dict)
+            return [(n, k, k, v) for n, k, v in pmc_rows(path, counter)]
+        out = []
         for name, did_vals in _pmc_by_dispatch(path, counter).items():
-            ids = sorted(did_vals, key=lambda x: int(x))[-last:]
-            per[name] = [did_vals[i] for i in ids]
-        return [(n, len(v), sum(v) / len(v)) for n, v in per.items()]
+            ids = sorted(did_vals, key=lambda x: int(x))
+            v = [did_vals[i] for i in ids[-last:]]
+            out.append((name, len(ids), len(v), sum(v) / len(v)))
+        return out
 
     f_rows = rows_of(fetch_path, "FETCH_SIZE")
     w_rows = rows_of(write_path, "WRITE_SIZE")
@@ -157,7 +159,9 @@ def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int, last
         m = [r for r in rows if sub in r[0]]
         if not m:
             raise SystemExit(f"no kernel matching {sub!r}")
-        return max(m, key=lambda r: r[1])          # most dispatches
+        # most dispatches in the whole run (with `last`, every kernel that ran
+        # at least `last` times averages the same number of them)
+        return max(m, key=lambda r: r[1])
 
     def copy_row(path, counter):
         # the single largest dispatch of a copy kernel: the calibration copy
@@ -169,14 +173,15 @@ def traffic(fetch_path: str, write_path: str, kernel: str, copy_bytes: int, last
                     best = (name, 1, v)
         return best
 
-    kf, kw = pick(f_rows, kernel), pick(w_rows, kernel)
+    kf = pick(f_rows, kernel)
+    kw = next((r for r in w_rows if r[0] == kf[0]), None) or pick(w_rows, kernel)
     cf, cw = copy_row(fetch_path, "FETCH_SIZE"), copy_row(write_path, "WRITE_SIZE")
     f_scale = copy_bytes / (cf[2] * 1024.0) if cf else 1.0
     w_scale = copy_bytes / (cw[2] * 1024.0) if cw else 1.0
-    fetch_b = kf[2] * 1024.0 * f_scale
-    write_b = kw[2] * 1024.0 * w_scale
-    return {"kernel": kf[0], "dispatches": kf[1], "fetch_kib_per_dispatch": kf[2],
-            "write_kib_per_dispatch": kw[2], "copy_kernel": cf[0] if cf else None,
+    fetch_b = kf[3] * 1024.0 * f_scale
+    write_b = kw[3] * 1024.0 * w_scale
+    return {"kernel": kf[0], "dispatches": kf[2], "fetch_kib_per_dispatch": kf[3],
+            "write_kib_per_dispatch": kw[3], "copy_kernel": cf[0] if cf else None,
             "copy_fetch_kib": cf[2] if cf else None, "copy_write_kib": cw[2] if cw else None,
             "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
             "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,

@@ -109,6 +109,8 @@ def test_default_value_tile(d, state, batch, heads, want):
     ("num_slots", (1 << 24) + 1, N.DL_ERR_INVALID_ARG),   # slot ids travel in 24 bits
     ("max_batch", 0, N.DL_ERR_INVALID_ARG),
     ("num_v_heads", 3, N.DL_ERR_INVALID_ARG),       # not a multiple of H_k = 2
+    ("num_v_heads", 65538, N.DL_ERR_INVALID_ARG),   # q/k head index exact up to 2^16 v-heads
+    ("num_slots", 1 << 24, N.DL_ERR_INVALID_ARG),     # with 128 v-heads: 2^31 (slot-head, tile) units
     ("num_k_heads", 0, N.DL_ERR_INVALID_ARG),
     ("merge_interval", 0, N.DL_ERR_INVALID_ARG),
     ("merge_interval", 65, N.DL_ERR_INVALID_ARG),
@@ -124,6 +126,8 @@ def test_descriptor_validation(field, value, code):
     setattr(desc, field, value)
     if field == "d_k":
         desc.d_v = value
+    if field == "num_slots" and value == 1 << 24:
+        desc.num_v_heads = 128
     with pytest.raises(dl.DeltaLogError) as ei:
         dl.dl_pool_sizes(desc)
     assert ei.value.code == code

@@ -107,17 +107,58 @@ def test_decode_grid_matches_the_launch():
 
 
 def test_decode_kernel_names_the_launched_kernel():
+    import dataclasses
     from workloads import CONFIGS
-    # the launcher's rule: d = 128, 16- or 32-column tiles, scalar or no decay
+    # the launcher's rule (narrow tiles, scalar or no decay, key chunks and
+    # value-side factor that fit the lane layout); the kernel traces name the
+    # same kernels for workloads 1 and 2
     assert bench.decode_kernel(CONFIGS[2], 16) == "dl_small_kernel"
     assert bench.decode_kernel(CONFIGS[2], 32) == "dl_small_kernel"
     assert bench.decode_kernel(CONFIGS[2], 64) == "dl_step_kernel"
     assert bench.decode_kernel(CONFIGS[4], 16) == "dl_step_kernel"      # per-key decay
-    assert bench.decode_kernel(CONFIGS[1], 16) == "dl_step_kernel"      # d = 16
+    assert bench.decode_kernel(CONFIGS[1], 16) == "dl_small_kernel"     # d = 16, fp32
+    assert bench.decode_kernel(dataclasses.replace(CONFIGS[1], in_dtype="bf16"), 16) == "dl_step_kernel"
     assert bench.decode_kernel(CONFIGS[5], 128) == "dl_step_kernel"
+    assert bench.decode_kernel(CONFIGS[5], 32) == "dl_small_kernel"     # bf16 tile, fp32 b: 8 x 4 bytes
+    # d = 32, bf16 inputs, 32-column tile: plain LA keeps b in bf16 (16 x 2
+    # bytes per lane), the delta rule in fp32 (16 x 4 bytes, over the limit)
+    assert bench.decode_kernel(dataclasses.replace(CONFIGS[1], d=32, in_dtype="bf16"), 32) == "dl_small_kernel"
+    assert bench.decode_kernel(dataclasses.replace(CONFIGS[2], d=32, in_dtype="bf16"), 32) == "dl_step_kernel"
+    assert bench.decode_kernel(dataclasses.replace(CONFIGS[2], d=64), 32) == "dl_small_kernel"
 
 
 def test_line_dtype_names_the_storage_of_16_bit_workloads():
     from workloads import CONFIGS
     assert bench.line_dtype(CONFIGS[2]) == "f32"
     assert bench.line_dtype(CONFIGS[5]).startswith("f32") and "bf16" in bench.line_dtype(CONFIGS[5])
+
+
+def test_traffic_averages_the_most_dispatched_matching_kernel(tmp_path):
+    # counter CSVs as rocprofv3 writes them: a torch conversion kernel whose
+    # name also contains "_kernel<" ran 70 times, the decode kernel 200 times;
+    # averaging the last 64 dispatches must not let the two tie
+    from linear_attention_recurrent_dl_amd.rocprof_summary import traffic
+    conv = "void at::native::vectorized_elementwise_kernel<4, bfloat16_copy_kernel_cuda>(int)"
+    dec = "void dl::dl_step_kernel<128, 128, 2, true, float, unsigned short, 0>(int, int, int, unsigned int)"
+    copy = "__amd_rocclr_copyBuffer"
+
+    def write(path, counter, conv_v, dec_first, dec_last, copy_v):
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        did = 0
+        for _ in range(70):
+            did += 1
+            rows.append(f'{did},"{conv}",{counter},{conv_v}')
+        did += 1
+        rows.append(f'{did},"{copy}",{counter},{copy_v}')
+        for i in range(200):
+            did += 1
+            rows.append(f'{did},"{dec}",{counter},{dec_first if i < 136 else dec_last}')
+        path.write_text("\n".join(rows) + "\n")
+
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    write(fp, "FETCH_SIZE", 1.0, 999.0, 100.0, 512.0)     # copy of 1 KiB reads half: scale 2
+    write(wp, "WRITE_SIZE", 1.0, 999.0, 10.0, 1024.0)
+    t = traffic(str(fp), str(wp), "_kernel<", 1024 * 1024, last=64)
+    assert t["kernel"] == dec and t["dispatches"] == 64
+    assert t["hbm_fetch_bytes_per_launch"] == 100.0 * 1024 * 2
+    assert t["hbm_write_bytes_per_launch"] == 10.0 * 1024
