@@ -78,6 +78,93 @@ __device__ __forceinline__ void ld_cols(const T *src, float (&x)[UPL]) {
     }
 }
 
+// ---- reduce-scatter across the lanes of a wave.  R values per lane are
+// summed over the lanes that differ only in the lane-index bits of MASK:
+// bits 5 and 4 by the row swaps, bits 3, 1 and 0 by DPP (bit 2 has no DPP
+// partner by exclusive-or).  A swap of two values hands each half of the
+// wave the sum of one of them, so every swap level halves the values a lane
+// holds for one swap and one add per pair; a DPP level does the same where
+// the select it needs saves instructions over the levels left.  Lanes whose
+// bit is 0 keep the sums of the even-numbered values, the others those of the
+// odd-numbered.  All lanes of the wave must be active.
+
+// instructions to sum r values over k DPP levels, halving where it pays
+constexpr int rs_best(int r, int k) {
+    if (k == 0) return 0;
+    if (r == 1) return k;
+    const int plain = r * k, split = 3 * (r / 2) + rs_best(r / 2, k - 1);
+    return plain < split ? plain : split;
+}
+constexpr bool rs_split_dpp(int r, int k) {
+    return r >= 2 && 3 * (r / 2) + rs_best(r / 2, k - 1) < r * k;
+}
+// DPP levels of MASK at bits <= bit
+constexpr int rs_dpp_levels(int mask, int bit) {
+    int k = 0;
+    for (int b = bit < 3 ? bit : 3; b >= 0; --b) k += (mask >> b) & 1;
+    return k;
+}
+// values per lane left after the levels of MASK, starting from r
+constexpr int rs_left(int r, int mask) {
+    for (int b = 5; b >= 0; --b) {
+        if (!((mask >> b) & 1)) continue;
+        if (b >= 4 ? r >= 2 : rs_split_dpp(r, rs_dpp_levels(mask, b))) r /= 2;
+    }
+    return r;
+}
+
+// x of lane ^ (1 << B) inside a row, B in {0, 1, 3}
+template <int B>
+__device__ __forceinline__ float from_lane_xor(float x) {
+    static_assert(B == 0 || B == 1 || B == 3, "exclusive-or partner by DPP");
+    if constexpr (B == 0) return dpp_f32<kDppQuadXor1>(x);
+    else if constexpr (B == 1) return dpp_f32<kDppQuadXor2>(x);
+    else return dpp_f32<kDppRowRor + 8>(x);
+}
+
+// Levels at bits BIT, BIT - 1, .., 0.  Returns the lane's offset: value m
+// left in the lane is the sum of original value m * 2^S' + offset, S' the
+// number of halving levels.
+template <int N, int R, int MASK, int BIT, int S>
+__device__ __forceinline__ int reduce_scatter(float (&x)[N], const int lane, const int sel) {
+    static_assert(!((MASK >> 2) & 1), "no exclusive-or partner for lane bit 2");
+    if constexpr (BIT < 0) {
+        return sel;
+    } else if constexpr (!((MASK >> BIT) & 1)) {
+        return reduce_scatter<N, R, MASK, BIT - 1, S>(x, lane, sel);
+    } else if constexpr (BIT >= 4) {
+        if constexpr (R >= 2) {
+#pragma unroll
+            for (int m = 0; m < R / 2; ++m) {
+                const uint32_t a = __float_as_uint(x[2 * m]), b = __float_as_uint(x[2 * m + 1]);
+                if constexpr (BIT == 5) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+                    x[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                } else {
+                    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+                    x[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                }
+            }
+            return reduce_scatter<N, R / 2, MASK, BIT - 1, S + 1>(x, lane, sel | (((lane >> BIT) & 1) << S));
+        } else {
+            x[0] = BIT == 5 ? sum_rows_xor2(x[0]) : sum_rows_xor1(x[0]);
+            return reduce_scatter<N, R, MASK, BIT - 1, S>(x, lane, sel);
+        }
+    } else if constexpr (rs_split_dpp(R, rs_dpp_levels(MASK, BIT))) {
+        const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+        for (int m = 0; m < R / 2; ++m) {
+            const float keep = hi ? x[2 * m + 1] : x[2 * m], send = hi ? x[2 * m] : x[2 * m + 1];
+            x[m] = keep + from_lane_xor<BIT>(send);
+        }
+        return reduce_scatter<N, R / 2, MASK, BIT - 1, S + 1>(x, lane, sel | ((int)hi << S));
+    } else {
+#pragma unroll
+        for (int m = 0; m < R; ++m) x[m] += from_lane_xor<BIT>(x[m]);
+        return reduce_scatter<N, R, MASK, BIT - 1, S>(x, lane, sel);
+    }
+}
+
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, bool EAGER>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
 dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gmag, const StepParams p) {
@@ -125,10 +212,18 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     const size_t gkC = (size_t)gk32 * (uint32_t)C;      // the q/k head's first key-log entry
     const uint32_t ek = (uint32_t)e * H_k + g;          // token row of q, k
     const uint32_t ev = (uint32_t)eh;                   // token row of v, lambda, beta, output
-    // tile geometry: the LPG lanes of a column group sit in one aligned run of
-    // a wave, so their partial sums close with DPP moves inside a row
-    constexpr int LPG = 64 / CG;
-    const int cg = lane / LPG, rg = wave * LPG + lane % LPG;
+    // tile geometry: a thread holds one 16-byte chunk (VEC columns) of RPT
+    // tile rows.  The column group sits in lane bits 2-3 (CG = 2: bit 2;
+    // CG = 8: bits 1-3), the wave's 64 / CG row groups in the others, so that
+    // the row sums reduce-scatter over lane bits 5, 4, 1 and 0 (row swaps and
+    // quad DPP); a 16-lane row still covers whole tile rows of contiguous bytes
+    static_assert(CG == 2 || CG == 4 || CG == 8, "column groups");
+    constexpr int LPG = 64 / CG;                        // row groups per wave
+    constexpr int CGB = CG == 8 ? 1 : 2;                // lowest lane bit of the column group
+    constexpr int CGL = CG == 2 ? 1 : (CG == 4 ? 2 : 3);
+    constexpr int TMASK = 0x3F & ~((CG - 1) << CGB);    // lane bits the row sums run over
+    const int cg = (lane >> CGB) & (CG - 1);
+    const int rg = wave * LPG + ((lane & ((1 << CGB) - 1)) | ((lane >> (CGB + CGL)) << CGB));
     const int jk = tid % TPE2;                          // the lane's place within its log entry
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
@@ -295,16 +390,35 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
             if (merge && i < n) stage_entry(i, kc, uu, w);
         }
         // sum over the wave's entries: lanes that agree modulo TPE2 hold the same columns
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            lq[u] = strided_sum<TPE2>(lq[u]);
-            if constexpr (DELTA) lk[u] = strided_sum<TPE2>(lk[u]);
-        }
-        if (lane < TPE2) {
+        if constexpr (TPE2 >= 8) {
+            // reduce-scatter over lane bits log2(TPE2) .. 5; every lane stores what it holds
+            constexpr int NR = DELTA ? 2 * UPL : UPL;
+            constexpr int EMASK = 0x3F & ~(TPE2 - 1);
+            float xs[NR];
 #pragma unroll
             for (int u = 0; u < UPL; ++u) {
-                s_part[1][wave][0][jk * UPL + u] = lq[u];
-                s_part[1][wave][1][jk * UPL + u] = lk[u];
+                xs[u] = lq[u];
+                if constexpr (DELTA) xs[UPL + u] = lk[u];
+            }
+            const int sel = reduce_scatter<NR, NR, EMASK, 5, 0>(xs, lane, 0);
+            constexpr int RL = rs_left(NR, EMASK);
+#pragma unroll
+            for (int m = 0; m < RL; ++m) {
+                const int t = m * (NR / RL) + sel;
+                s_part[1][wave][t / UPL][jk * UPL + t % UPL] = xs[m];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < UPL; ++u) {
+                lq[u] = strided_sum<TPE2>(lq[u]);
+                if constexpr (DELTA) lk[u] = strided_sum<TPE2>(lk[u]);
+            }
+            if (lane < TPE2) {
+#pragma unroll
+                for (int u = 0; u < UPL; ++u) {
+                    s_part[1][wave][0][jk * UPL + u] = lq[u];
+                    s_part[1][wave][1][jk * UPL + u] = lk[u];
+                }
             }
         }
     }
@@ -324,16 +438,23 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
             if constexpr (DELTA) acck[c] += x[c] * kd;
         }
     }
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-        accq[c] = group_sum<LPG>(accq[c]);
-        if constexpr (DELTA) acck[c] = group_sum<LPG>(acck[c]);
-    }
-    if (lane % LPG == 0) {
+    {
+        // row sums of y~_q (and y~_k) on the thread's VEC columns, scattered
+        // over the lanes of the column group; every lane stores what it holds
+        // (lanes holding the same sum store the same value)
+        constexpr int NV = DELTA ? 2 * VEC : VEC;
+        float xs[NV];
 #pragma unroll
         for (int c = 0; c < VEC; ++c) {
-            s_part[0][wave][0][cg * VEC + c] = accq[c];
-            s_part[0][wave][1][cg * VEC + c] = acck[c];
+            xs[c] = accq[c];
+            if constexpr (DELTA) xs[VEC + c] = acck[c];
+        }
+        const int sel = reduce_scatter<NV, NV, TMASK, 5, 0>(xs, lane, 0);
+        constexpr int RL = rs_left(NV, TMASK);
+#pragma unroll
+        for (int m = 0; m < RL; ++m) {
+            const int t = m * (NV / RL) + sel;          // value index: t / VEC = q or k, t % VEC = column
+            s_part[0][wave][t / VEC][cg * VEC + t % VEC] = xs[m];
         }
     }
     // a . q, from the first entry's lanes, in lanes 0-15 (the column lanes)
