@@ -78,7 +78,7 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *                   1 <= P <= 2^24, and P * num_v_heads * (d_k / value_tile)
  *                   below 2^31 (the kernels index value tiles in 32 bits)
  *   max_batch       largest B of one dl_decode_step / dl_slot_assign / dl_merge
- *   num_v_heads     H_v <= 65536;  num_k_heads H_k (H_v % H_k == 0; grouped
+ *   num_v_heads     H_v <= 32768;  num_k_heads H_k (H_v % H_k == 0; grouped
  *                   value heads)
  *   d_k, d_v        head dims; the library supports d_k == d_v in {16, 32, 64, 128}
  *   merge_interval  L = [DL]'s M: one merge every L decodes of a slot; the log

@@ -77,9 +77,9 @@ int validate_desc(const dl_pool_desc *d) {
         return fail(DL_ERR_INVALID_ARG, "num_v_heads (%d) must be a multiple of num_k_heads (%d)",
                     d->num_v_heads, d->num_k_heads);
     // the kernels take a v-head's q/k head as the high word of
-    // h * ceil(2^32 / (H_v / H_k)), exact while h * (H_v / H_k) < 2^32
-    if (d->num_v_heads > 65536)
-        return fail(DL_ERR_INVALID_ARG, "num_v_heads (%d) must be at most 65536", d->num_v_heads);
+    // 2h * ceil(2^31 / (H_v / H_k)), exact while h * (H_v / H_k) < 2^31
+    if (d->num_v_heads > 32768)
+        return fail(DL_ERR_INVALID_ARG, "num_v_heads (%d) must be at most 32768", d->num_v_heads);
     if (d->merge_interval < 1 || d->merge_interval > dl::kMaxLogCap + 1)
         return fail(DL_ERR_INVALID_ARG, "merge_interval must be in [1, %d] (got %d)", dl::kMaxLogCap + 1,
                     d->merge_interval);

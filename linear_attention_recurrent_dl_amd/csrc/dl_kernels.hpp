@@ -193,6 +193,22 @@ __device__ __forceinline__ int xcd_unit(int bid, int nb) {
     if ((nb & 7) != 0) return bid;
     return (bid & 7) * (nb >> 3) + (bid >> 3);
 }
+__device__ __forceinline__ uint32_t xcd_unit_u(uint32_t bid, uint32_t nb) {
+    if ((nb & 7) != 0) return bid;
+    return (bid & 7) * (nb >> 3) + (bid >> 3);
+}
+
+// q/k head of v-head h: h / (H_v / H_k) as the high word of 2h * gdiv, with
+// gdiv = ceil(2^31 / (H_v / H_k)) from the host.  Exact while
+// h * (gdiv * (H_v / H_k) - 2^31) < 2^31, which holds for H_v <= 32768 (the
+// pool refuses more); gdiv = 2^31 gives h itself.  No branch, no division.
+__device__ __forceinline__ uint32_t qk_head(uint32_t h, uint32_t gdiv) { return __umulhi(h + h, gdiv); }
+// h is the first v-head of its q/k group (the group's key-factor writer):
+// its q/k head differs from that of h - 1.  At h = 0 the unsigned 2h - 2
+// wraps to 2^32 - 2, whose high word gdiv - 1 is not 0.
+__device__ __forceinline__ bool first_of_group(uint32_t h, uint32_t gdiv) {
+    return __umulhi(h + h, gdiv) != __umulhi(h + h - 2u, gdiv);
+}
 
 // Block geometry: a block owns the D x BV value tile of one (slot, v-head)
 // ([DL] GPU-execution section: work units own d_k x B_V tiles, N_V = d_v / B_V).
@@ -306,7 +322,7 @@ __device__ __forceinline__ void replay_coefficients(int tid, int n, bool merge, 
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
-dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gmag, const StepParams p) {
+dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gdiv, const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
@@ -362,17 +378,14 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     extern __shared__ float4 s_dyn[];
 
     // The launch geometry comes as leading scalar arguments (head counts, log
-    // capacity, the q/k-head divisor), which the build preloads into registers
+    // capacity, the q/k-head multiplier), which the build preloads into registers
     // before the block starts, so the block's slot word can be fetched at
     // once.  The grid has one row per batch entry (blockIdx.y); along x run
     // the entry's (v-head, value tile) units, numbered so that each XCD holds
     // a contiguous run of them.  No integer division: a wave issues one
     // instruction per four cycles, and a division by a run-time value costs
     // about 25 of them ahead of the first load.  The q/k head of v-head h is
-    // h / (H_v / H_k), taken as the high word of h * gmag with
-    // gmag = ceil(2^32 / (H_v / H_k)) (exact for H_v <= 2^16: the error term
-    // h * (gmag * (H_v / H_k) - 2^32) stays below 2^32), or h when gmag = 0
-    // (one v-head per q/k head).
+    // h / (H_v / H_k), from a host-computed multiplier (qk_head).
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int ux = xcd_unit(blockIdx.x, H_v * NV);
@@ -380,9 +393,9 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     const int h = ux / NV, vt = ux - h * NV;            // v-head, value tile
     const int eh = e * H_v + h;                         // (entry, v-head)
     const int c0 = vt * BV;                             // first column of the tile
-    const int g = gmag ? (int)__umulhi((uint32_t)h, gmag) : h;
+    const int g = (int)qk_head((uint32_t)h, gdiv);
     // the first v-head of its q/k group writes the group's key factor
-    const bool kwriter = h == 0 || gmag == 0 || (int)__umulhi((uint32_t)(h - 1), gmag) != g;
+    const bool kwriter = first_of_group((uint32_t)h, gdiv);
     const uint32_t sword = p.slots[e];
     // Every other argument the block reads is fetched now, with the slot
     // word, in one batch: left to itself the compiler loads each where first
@@ -1110,8 +1123,8 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     if (mode != MODE_EAGER && p.C < 1) return hipErrorInvalidValue;    // the log kernels need a log
     const dim3 grid(per_entry, p.nunits / per_entry);
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
-    if (grp > 1 && p.H_v > 65536) return hipErrorInvalidValue;         // gmag exact below
-    const uint32_t gmag = grp == 1 ? 0u : (uint32_t)((0x100000000ull + grp - 1) / grp);
+    if (p.H_v > 32768) return hipErrorInvalidValue;                   // qk_head exact below
+    const uint32_t gdiv = (uint32_t)((0x80000000ull + grp - 1) / grp);
     // narrow tiles with a scalar or no decay: decode and eager steps run the
     // one-barrier kernel where its lane layout fits (at least 4 key chunks per
     // entry, every thread owning tile rows, at most 32 bytes of value factor
@@ -1123,21 +1136,21 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     switch (mode) {
     case MODE_STEP:
         if constexpr (NARROW)
-            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, false><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, false><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         else
-            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         break;
     case MODE_EAGER:
         if constexpr (NARROW)
-            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, true><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, true><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         else
-            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         break;
     case MODE_MERGE:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         break;
     case MODE_STEP_SPLIT:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gmag, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         break;
     default:
         return hipErrorInvalidValue;

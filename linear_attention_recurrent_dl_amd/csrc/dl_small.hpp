@@ -167,7 +167,7 @@ __device__ __forceinline__ int reduce_scatter(float (&x)[N], const int lane, con
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, bool EAGER>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
-dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gmag, const StepParams p) {
+dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gdiv, const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
@@ -177,11 +177,10 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     constexpr int TPE2 = CPE / 2;                 // lanes per log entry (two chunks each)
     constexpr int EPR = NT / TPE2;                // log entries per round
     constexpr int UPL = BV / TPE2;                // value-factor columns per lane
-    constexpr int UV = 16 / (int)sizeof(BT);      // value-factor elements per 16-byte store
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
     static_assert(DECAY != DECAY_PER_KEY, "scalar or no decay");
     static_assert(!G::RAGGED && RPT * RG == D, "tile rows");
-    static_assert(UPL >= 1 && UPL * sizeof(BT) <= 32 && BV % UV == 0, "value-factor columns");
+    static_assert(UPL >= 1 && UPL * sizeof(BT) <= 32, "value-factor columns");
     static_assert(TPE2 >= 2 && TPE2 <= 64 && 64 % TPE2 == 0, "entry lanes within a wave");
 
     // partial projections per wave: [tile, log][wave][q, k][column], read
@@ -194,14 +193,16 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int ux = xcd_unit(blockIdx.x, H_v * NV);
-    const int e = blockIdx.y;                           // batch entry of this launch
-    const int h = ux / NV, vt = ux - h * NV;            // v-head, value tile
-    const int eh = e * H_v + h;
-    const int c0 = vt * BV;                             // first column of the tile
-    const int g = gmag ? (int)__umulhi((uint32_t)h, gmag) : h;
-    const bool kwriter = h == 0 || gmag == 0 || (int)__umulhi((uint32_t)(h - 1), gmag) != g;
+    // (unsigned index math with no branch: the argument fetch below then
+    // shares a block with it, and the scheduler issues the fetch first)
+    const uint32_t e = blockIdx.y;                      // batch entry of this launch
     const uint32_t sword = p.slots[e];
+    const uint32_t ux = xcd_unit_u(blockIdx.x, (uint32_t)H_v * NV);
+    const int h = (int)(ux / NV), vt = (int)(ux % NV);  // v-head, value tile
+    const int eh = (int)e * H_v + h;
+    const int c0 = vt * BV;                             // first column of the tile
+    const int g = (int)qk_head((uint32_t)h, gdiv);
+    const bool kwriter = first_of_group((uint32_t)h, gdiv);
     asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
                  "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(sword));
     const uint32_t slot = sword & kSlotMask;
@@ -227,15 +228,18 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     const int jk = tid % TPE2;                          // the lane's place within its log entry
     const bool owner = vt == 0;                         // writes the tile-shared log metadata
 
-    // output and appended value factor: NO lanes cover 4 output columns each,
-    // then NU lanes one value-factor chunk (UV columns) each
-    constexpr int NO = BV / 4;
-    constexpr int NU = EAGER ? 0 : BV / UV;
-    constexpr int MC = UV > 4 ? UV : 4;
-    static_assert(NO + NU <= 64, "column lanes fit one wave");
-    const bool is_u = tid >= NO;
-    const int cb = is_u ? min(tid - NO, (NU > 0 ? NU : 1) - 1) * UV : tid * 4;   // first column (clamped)
-    const int nc = is_u ? UV : 4;
+    // output and appended value factor, one column per lane of wave 0.  The
+    // partial sums are read back as float4 slots (a q/k row of BV / 4 slots,
+    // C4B lane bits, then the q/k bit) and reduce-scattered over the lane bits
+    // above, so that lane l ends with y~_q (q/k bit 0) or y~_k (bit 1) of
+    // column 4 (l mod BV/4) + (lane bit 5) + 2 (lane bit 4).  Lanes whose other
+    // bits (bit 3 at 16 columns) are 0 own their column.
+    constexpr int C4B = BV == 16 ? 2 : 3;
+    static_assert(BV == 4 << C4B, "16 or 32 columns");
+    constexpr int SMASK = 0x3F & ~((2 << C4B) - 1);    // lane bits the slot sums run over
+    const bool oq = !((lane >> C4B) & 1);               // holds y~_q: output lane, else value-factor lane
+    const bool oown = (lane & SMASK & 0x0F) == 0;
+    const int ocol = 4 * (lane & ((1 << C4B) - 1)) + ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1);
 
     // ---- loads, all issued before any is consumed (v of the lane's output
     // columns too: a load only the output lanes consume would be sunk behind
@@ -266,16 +270,7 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
         qr[j] = to_f32(qg[rg + RG * j]);
         kr[j] = to_f32(kg[rg + RG * j]);
     }
-    float vc[MC];
-    {
-        const IT *vg = reinterpret_cast<const IT *>(p.v) + ev * D + c0 + cb;
-        if constexpr (MC == 4) {
-            ld_cols<IT, 4>(vg, vc);                     // one 16- or 8-byte load
-        } else {
-#pragma unroll
-            for (int c = 0; c < MC; ++c) vc[c] = to_f32(vg[c < nc ? c : 0]);
-        }
-    }
+    const float vo = to_f32(reinterpret_cast<const IT *>(p.v)[ev * D + c0 + ocol]);   // v on the lane's column
     uint4 qc[2], ac[2];                                 // q and a on the lane's two key chunks
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -478,16 +473,14 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
     }
     __syncthreads();
 
-    // ---- output and appended value factor (wave 0).  Each lane reads float4
-    // slot(s) of the partial sums; lanes that agree modulo NQ hold the same
-    // (q or k, 4 columns), whose sources and waves the row swaps then add:
-    // lane j < BV/4 ends with y~_q on columns 4j.., lane BV/4 + j with y~_k.
+    // ---- output and appended value factor (wave 0), one column per lane
     if (wave != 0) {
         if (!merge) return;
     } else {
     constexpr int NSL = 2 * NW * NQ;                   // slots
     constexpr int SPL = (NSL + 63) / 64;               // slots per lane
-    static_assert(64 % NQ == 0, "partial-sum slots");
+    static_assert(64 % NQ == 0 && NQ == 2 << C4B, "partial-sum slots");
+    static_assert(rs_left(4, SMASK) == 1, "one column per lane");
     const float4 *slots = reinterpret_cast<const float4 *>(&s_part[0][0][0][0]);
     float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -498,49 +491,24 @@ dl_small_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uin
             r[0] += a.x; r[1] += a.y; r[2] += a.z; r[3] += a.w;
         }
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r[c] = strided_sum<NQ>(r[c]);
-    // y~_k of an output lane's columns sits BV/4 lanes up, in the same row
+    // sources and waves summed, the four columns scattered over lane bits 5, 4
+    reduce_scatter<4, 4, SMASK, 5, 0>(r, lane, 0);
+    const float y = r[0];
+    // y~_k of an output lane's column sits BV/4 lanes up, in the same row
     // (moved while every lane of the wave is active: DPP reads no lane that
-    // EXEC disables)
-    float yka[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(r[c]), 0x100 + BV / 4,
-                                                                   0xf, 0xf, false));
-        yka[c] = is_u ? r[c] : up;
-    }
-    if (tid < NO || (tid < NO + NU && !merge)) {
-        float ov[MC], bc[MC];
-#pragma unroll
-        for (int c4 = 0; c4 < MC; c4 += 4) {
-            if (c4 < nc) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float b = DELTA ? beta * (vc[c4 + j] - yka[j]) : vc[c4 + j];
-                    bc[c4 + j] = b;
-                    ov[c4 + j] = r[j] + aq * b;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bc[c4 + j] = ov[c4 + j] = 0.f;
-            }
+    // EXEC disables); a . q from lane 0
+    const float yup = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x100 + BV / 4, 0xf, 0xf, false));
+    const float aqs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(aq), 0));
+    const float b = DELTA ? beta * (vo - (oq ? yup : y)) : vo;
+    if (oown) {
+        if (oq) {
+            if (merge) s_b[ocol] = b;
+            __builtin_nontemporal_store(y + aqs * b, reinterpret_cast<float *>(p.out) + (size_t)ev * D + c0 + ocol);
+        } else if (!EAGER && !merge) {
+            // (a cached store: the next steps read the entry back, and a
+            // streaming store measured 0.6% slower at batch 1)
+            reinterpret_cast<BT *>(p.ulog)[(shC + n) * D + c0 + ocol] = from_f32<BT>(b);
         }
-        if (merge && !is_u) *reinterpret_cast<float4 *>(&s_b[cb]) = make_float4(bc[0], bc[1], bc[2], bc[3]);
-        const uint4 wo = make_uint4(__float_as_uint(ov[0]), __float_as_uint(ov[1]), __float_as_uint(ov[2]),
-                                    __float_as_uint(ov[3]));
-        uint4 wu = wo;
-        if constexpr (!EAGER) {
-            float ub4[UV];
-#pragma unroll
-            for (int c = 0; c < UV; ++c) ub4[c] = bc[c];
-            wu = pack_16<BT, UV>(ub4);
-        }
-        char *dst = is_u ? reinterpret_cast<char *>(p.ulog) + ((shC + n) * D + c0 + cb) * sizeof(BT)
-                         : reinterpret_cast<char *>(p.out) + ((size_t)ev * D + c0 + cb) * sizeof(float);
-        // per-component select: a select of whole vectors goes through scratch
-        st16_stream(dst, 0, make_uint4(is_u ? wu.x : wo.x, is_u ? wu.y : wo.y, is_u ? wu.z : wo.z,
-                                       is_u ? wu.w : wo.w));
     }
     if (!merge) return;
     }

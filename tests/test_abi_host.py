@@ -109,7 +109,7 @@ def test_default_value_tile(d, state, batch, heads, want):
     ("num_slots", (1 << 24) + 1, N.DL_ERR_INVALID_ARG),   # slot ids travel in 24 bits
     ("max_batch", 0, N.DL_ERR_INVALID_ARG),
     ("num_v_heads", 3, N.DL_ERR_INVALID_ARG),       # not a multiple of H_k = 2
-    ("num_v_heads", 65538, N.DL_ERR_INVALID_ARG),   # q/k head index exact up to 2^16 v-heads
+    ("num_v_heads", 32770, N.DL_ERR_INVALID_ARG),   # q/k head index exact up to 2^15 v-heads
     ("num_slots", 1 << 24, N.DL_ERR_INVALID_ARG),     # with 128 v-heads: 2^31 (slot-head, tile) units
     ("num_k_heads", 0, N.DL_ERR_INVALID_ARG),
     ("merge_interval", 0, N.DL_ERR_INVALID_ARG),
@@ -329,3 +329,20 @@ def test_decode_window_rules():
     assert lib.dl_decode_window(q.handle, 1, op, 2, None, None, None, 16, None, None, None) == N.DL_ERR_INVALID_ARG
     assert lib.dl_decode_window(q.handle, 1, op, 2, None, None, None, None, 16, None, None) == N.DL_ERR_INVALID_ARG
     assert lib.dl_decode_window(q.handle, 0, op, 2, None, None, None, None, None, None, None) == N.DL_OK
+
+
+def test_qk_head_multiplier_is_exact_up_to_the_head_limit():
+    """The kernels find the q/k head of v-head h as the high word of
+    2h * ceil(2^31 / G), G = H_v / H_k, and the group's first v-head as the
+    one whose q/k head differs from that of h - 1 (unsigned, so h = 0 wraps).
+    Checked over every h for group sizes up to the pool's 32768 v-heads."""
+    import numpy as np
+    limit = 32768
+    for G in sorted({1, 2, 3, 5, 7, 8, 16, 31, 127, 1000, 4095, 4096, 16383, 32767, 32768}):
+        H_v = (limit // G) * G
+        m = (2 ** 31 + G - 1) // G
+        h = np.arange(H_v, dtype=np.uint64)
+        g = ((2 * h) * m) >> np.uint64(32)
+        assert np.array_equal(g, h // G), G
+        prev = (((2 * h - 2) % 2 ** 32) * m) >> np.uint64(32)
+        assert np.array_equal(g != prev, h % G == 0), G
