@@ -433,12 +433,13 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
 
     // ---- 1. every load of the block is issued before any is consumed: the
     //         token inputs (while the counter is in flight), the whole live
-    //         log, then the base tile.  In narrow-tile decode launches every
-    //         lane issues the token loads alike (clamped indices, values used
-    //         by the lanes that need them), which keeps the in-order wait
-    //         counts exact: the wait for the snapshots below then lets the
-    //         later loads stay in flight.  Elsewhere only the lanes that use
-    //         them load.
+    //         log, then the base tile.  Every lane issues the token loads
+    //         alike (indices taken modulo d, values used by the lanes below
+    //         d).  Under a branch, the 16-bit inputs' widening to fp32 made the
+    //         compiler wait for them at the branch's end, a whole memory round
+    //         trip before the log and tile loads were issued; and in
+    //         narrow-tile launches the in-order wait counts stay exact, so the
+    //         wait for the snapshots below lets the later loads stay in flight.
     float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
     float lp0 = 0.f;                                    // l' (narrow tiles with a scalar decay: every lane)
     IT kraw{};
@@ -452,10 +453,7 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         if constexpr (PERKEY) lam = p.lam[ev * D + (tid % D)];
         if constexpr (DELTA) beta = p.beta[ev];
     };
-    if constexpr (TOKEN) {
-        if constexpr (SMALL) token_loads();
-        else if (tid < D) token_loads();
-    }
+    if constexpr (TOKEN) token_loads();
     const IT *klog = reinterpret_cast<const IT *>(p.klog);
     const BT *ulog = reinterpret_cast<const BT *>(p.ulog);
     const float *lamlog = p.lamlog;
