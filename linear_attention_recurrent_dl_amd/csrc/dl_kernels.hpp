@@ -442,13 +442,12 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     //         wait for the snapshots below lets the later loads stay in flight.
     float qv = 0.f, kv = 0.f, vv = 0.f, lam = 0.f, lbar = 0.f, beta = 0.f, lam_i = 0.f;
     float lp0 = 0.f;                                    // l' (narrow tiles with a scalar decay: every lane)
-    IT kraw{};
+    IT qraw{}, kraw{}, vraw{};                          // as stored; widened after the tile loads
     auto token_loads = [&]() {
         const uint32_t qo = ek * D + (tid % D);
-        qv = to_f32(reinterpret_cast<const IT *>(p.q)[qo]);
+        qraw = reinterpret_cast<const IT *>(p.q)[qo];
         kraw = reinterpret_cast<const IT *>(p.k)[qo];
-        kv = to_f32(kraw);
-        vv = to_f32(reinterpret_cast<const IT *>(p.v)[ev * D + c0 + (tid % BV)]);
+        vraw = reinterpret_cast<const IT *>(p.v)[ev * D + c0 + (tid % BV)];
         if constexpr (SCALAR) lam = p.lam[ev];
         if constexpr (PERKEY) lam = p.lam[ev * D + (tid % D)];
         if constexpr (DELTA) beta = p.beta[ev];
@@ -665,6 +664,16 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     for (int j = 0; j < RPT; ++j) {
         if (!G::RAGGED || rg + RG * j < D) tile[j] = ld16(tbase, toff + j * TROW);
         else tile[j] = make_uint4(0, 0, 0, 0);
+    }
+    // 16-bit token inputs are widened only now, behind a scheduling barrier
+    // at d = 128: widened earlier, the compiler waited for them ahead of the
+    // tile loads (KDA-style batch 128: 2% per step, the serving pool 1%).  At
+    // d = 64 the barrier measured slower (GLA-style eager kernel 19%).
+    if constexpr (TOKEN) {
+        if constexpr (sizeof(IT) == 2 && D >= 128) __builtin_amdgcn_sched_barrier(0);
+        qv = to_f32(qraw);
+        kv = to_f32(kraw);
+        vv = to_f32(vraw);
     }
 
     // ---- 2. decay bookkeeping, decayed q / k, and the log into LDS
