@@ -90,8 +90,10 @@ enum { DL_F32 = 0, DL_BF16 = 1 };
  *   value_tile      B_V, columns of the d_k x B_V value tile one GPU work unit
  *                   owns ([DL] GPU-execution section, value tiling); 0 picks the
  *                   library default from u = max_batch * num_v_heads: d when
- *                   u >= 256 or d <= 32; else, at d = 128, 16 when u < 64 and
- *                   64 when u >= 128 with an fp32 state; else 32.  A default
+ *                   u >= 256 or d <= 32, except 64 at d = 128 for a bf16 state
+ *                   with L > 1 and a scalar or no decay while u < 2048; below
+ *                   u = 256, at d = 128, 16 when u < 64 and 64 when u >= 128
+ *                   with an fp32 state; else 32.  A default
  *                   whose live log would exceed the LDS staging budget is
  *                   halved until it fits or reaches the narrowest built width.
  *                   Built widths: d = 128: 128, 64, 32, 16; d = 64: 64, 32;

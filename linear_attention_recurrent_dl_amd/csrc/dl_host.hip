@@ -56,7 +56,8 @@ bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 int value_tile_of(const dl_pool_desc *d) {
     if (d->value_tile) return d->value_tile;
-    int bv = dl::default_value_tile(d->d_k, d->state_dtype, (long long)d->max_batch * d->num_v_heads);
+    int bv = dl::default_value_tile(d->d_k, d->state_dtype, (long long)d->max_batch * d->num_v_heads, d->decay,
+                                    d->merge_interval);
     // a default whose live log would not fit the LDS staging budget falls back
     // to the widest narrower tile that does (the value factors shrink with it)
     while (dl::value_tile_supported(d->d_k, bv / 2) &&

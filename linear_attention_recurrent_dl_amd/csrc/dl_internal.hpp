@@ -127,12 +127,19 @@ inline size_t log_stage_bytes(int D, int BV, int C, int decay, int update, int i
 // launches spread one step over more CUs with narrower tiles: 16 columns for
 // 63 slot-heads or fewer at d = 128 (about 2% faster than 32 for 32
 // slot-heads), then 32, and for fp32 d = 128 also 64 below 256 slot-heads, so
-// that a launch keeps at least 256 blocks.
-inline int default_value_tile(int D, int state_dtype, long long units) {
+// that a launch keeps at least 256 blocks.  A bf16 state with a log (L > 1)
+// and a scalar or no decay takes 64 columns up to 2047 slot-heads: half-size
+// tiles double the blocks of a launch that is one round of whole rows, which
+// measured 8% faster per step at 1024 slot-heads and 1.6% at 2048 (GDN,
+// d = 128), while fp32 states and the eager kernel (L = 1) measured the same
+// or faster with whole rows.
+inline int default_value_tile(int D, int state_dtype, long long units, int decay, int L) {
     if (D < 64) return D;
     if (D == 128 && units < 64) return 16;
     if (D == 128 && state_dtype != BF16 && units >= 128 && units < 256) return 64;
-    return units < 256 ? 32 : D;
+    if (units < 256) return 32;
+    if (D == 128 && state_dtype == BF16 && L > 1 && decay != DECAY_PER_KEY && units < 2048) return 64;
+    return D;
 }
 // The window kernel stages token inputs in LDS kWindowChunk steps at a time,
 // double buffered: per buffer q, a [K][D], e^{lambda} [K][D] (per-key decay),

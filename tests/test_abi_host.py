@@ -97,11 +97,22 @@ def test_value_tile_choices(d, bv, ok):
     (16, "f32", 1, 2, 16)])
 def test_default_value_tile(d, state, batch, heads, want):
     """Narrow tiles while a launch's slot-heads would give fewer than 256
-    blocks, whole rows beyond."""
+    blocks, whole rows beyond (per-key decay; fp32 and eager pools alike)."""
     desc = dl.make_desc(batch, batch, heads, heads, d, 16, "per_key", "delta", state, "f32")
     assert dl.dl_value_tile(desc) == want
-    assert dl.dl_value_tile(dl.make_desc(batch, batch, heads, heads, d, 16, "scalar", "delta", state,
+    assert dl.dl_value_tile(dl.make_desc(batch, batch, heads, heads, d, 1, "scalar", "delta", state,
                                          "bf16")) == want
+
+
+@pytest.mark.parametrize("batch,want", [(1, 16), (4, 32), (8, 64), (32, 64), (63, 64), (64, 128), (256, 128)])
+def test_default_value_tile_bf16_state_with_log(batch, want):
+    """A bf16 state with a log and a scalar decay keeps 64-column tiles up to
+    2047 slot-heads (32 v-heads here); an eager pool (L = 1) of the same shape
+    takes whole rows from 256 slot-heads."""
+    desc = dl.make_desc(batch, batch, 32, 16, 128, 16, "scalar", "delta", "bf16", "bf16")
+    assert dl.dl_value_tile(desc) == want
+    eager = dl.make_desc(batch, batch, 32, 16, 128, 1, "scalar", "delta", "bf16", "bf16")
+    assert dl.dl_value_tile(eager) == (want if batch * 32 < 256 else 128)
 
 
 @pytest.mark.parametrize("field,value,code", [
