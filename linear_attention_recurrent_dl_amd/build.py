@@ -37,11 +37,12 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list:
-    # kernarg preload: the decode kernel's leading scalar arguments (launch
-    # geometry) arrive in registers, no scalar load ahead of its first fetch
+    # kernarg preload: the decode kernel's leading arguments (launch geometry,
+    # the first slot of a consecutive launch, the base and counter pointers:
+    # 10 dwords) arrive in registers, no scalar load ahead of its first fetch
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-mllvm", "-amdgpu-kernarg-preload-count=4",
+            "-mllvm", "-amdgpu-kernarg-preload-count=10",
             "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

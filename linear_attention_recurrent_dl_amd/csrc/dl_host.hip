@@ -263,6 +263,14 @@ int copy_states(dl_pool *pool, int32_t n, const int32_t *ids, void *ext, bool to
     return dl::launch_chunks(n, dl::kMaxLaunchSlots, launch, commit);
 }
 
+// First slot of a launch whose cnt slots are consecutive, else kGathered
+// (its blocks then read their slot words).
+uint32_t consecutive_slot0(const int32_t *ids, int32_t cnt) {
+    for (int32_t j = 1; j < cnt; ++j)
+        if (ids[j] != ids[0] + j) return dl::kGathered;
+    return (uint32_t)ids[0];
+}
+
 // Shared by dl_decode_step, dl_eager_step and dl_decode_step_noalloc.  The
 // split-replay coefficients of a launch go to `coef` (the pool's buffer, or
 // the static scratch), launches carry at most `chunk` slots.
@@ -322,6 +330,12 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
                 for (int32_t j = 0; j < cnt; ++j)
                     p.slots[j] |= (cap ? dl::kNoHint : (uint32_t)pool->n[ids[lo + j]]) << dl::kSlotBits;
             }
+            // A recorded decode launch of consecutive slots names its first:
+            // the blocks then know their slots without an argument fetch.  A
+            // direct one keeps its slot words, which carry the host's live
+            // lengths.
+            p.slot0 = (mode == dl::MODE_STEP && cap) ? consecutive_slot0(ids + lo, cnt) : dl::kGathered;
+            const int kmode = p.slot0 != dl::kGathered ? dl::MODE_STEP_CONSEC : mode;
             if (split) {
                 // ReplayPrep, one block per (entry, v-head), into the coefficient scratch
                 p.nunits = cnt * d.num_v_heads;
@@ -330,7 +344,7 @@ int decode(dl_pool *pool, int32_t B, const int32_t *ids, const void *q, const vo
                 if (e != hipSuccess) return hip_fail((hipError_t)e, "replay-prep kernel launch");
             }
             p.nunits = cnt * d.num_v_heads * pool->nv;
-            const int e = dl::launch_step(d.d_k, pool->bv, mode, d.decay, d.update, d.state_dtype, d.in_dtype, p,
+            const int e = dl::launch_step(d.d_k, pool->bv, kmode, d.decay, d.update, d.state_dtype, d.in_dtype, p,
                                           shmem, (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail((hipError_t)e, "decode kernel launch");
             return DL_OK;
@@ -366,6 +380,7 @@ int merge_slots(dl_pool *pool, int32_t n, const int32_t *ids, void *stream) {
         if (pool->dry || C == 0) return DL_OK;     // no log to merge in an eager pool
         p.nunits = cnt * d.num_v_heads * pool->nv;
         memcpy(p.slots, ids + lo, cnt * sizeof(int32_t));
+        p.slot0 = dl::kGathered;
         const int e = dl::launch_step(d.d_k, pool->bv, dl::MODE_MERGE, d.decay, d.update, d.state_dtype,
                                       d.in_dtype, p, shmem, (hipStream_t)stream);
         return e != hipSuccess ? hip_fail((hipError_t)e, "merge kernel launch") : DL_OK;

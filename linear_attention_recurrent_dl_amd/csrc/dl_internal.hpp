@@ -24,6 +24,8 @@ constexpr int kMaxSlots = 1 << kSlotBits;
 // Top byte of a decode launch's slot word when the host gives no live length
 // (launches recorded into a graph, whose replays may start at any phase).
 constexpr uint32_t kNoHint = 0xFF;
+// StepParams::slot0 of a launch whose blocks read their slot words.
+constexpr uint32_t kGathered = 0xFFFFFFFFu;
 
 enum Mode : int {
     MODE_STEP = 0,   // DeltaLog decode: append, or merge when the log is full
@@ -31,6 +33,7 @@ enum Mode : int {
     MODE_MERGE = 2,  // materialize base + log, no token
     MODE_STEP_SPLIT = 3,  // MODE_STEP whose appending units read ReplayPrep's coefficients
     MODE_REPLAY_PREP = 4, // ReplayPrep: key-side coefficients once per (entry, v-head)
+    MODE_STEP_CONSEC = 5, // MODE_STEP over consecutive slots (slot0, slot0 + 1, ..), no host live lengths
 };
 
 enum DType : int { F32 = 0, BF16 = 1 };
@@ -56,6 +59,7 @@ struct StepParams {
     int32_t C;           // log capacity L - 1
     int32_t NV;          // value tiles per slot-head
     int32_t nunits;      // blocks in this launch = n * H_v * (d_v / B_V), or n * H_v (ReplayPrep)
+    uint32_t slot0;      // first slot of a MODE_STEP_CONSEC launch, else kGathered
     uint32_t slots[kMaxLaunchSlots];   // slot words (see kSlotBits)
 };
 

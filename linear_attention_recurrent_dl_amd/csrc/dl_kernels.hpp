@@ -322,7 +322,8 @@ __device__ __forceinline__ void replay_coefficients(int tid, int n, bool merge, 
 
 template <int D, int BV, int DECAY, bool DELTA, typename ST, typename IT, int MODE>
 __global__ void __launch_bounds__((Tile<D, BV, ST>::NT))
-dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gdiv, const StepParams p) {
+dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint32_t gdiv, const uint32_t slot0,
+               void *const base, int32_t *const nlog, const StepParams p) {
     using G = Tile<D, BV, ST>;
     using BT = typename std::conditional<DELTA, float, IT>::type;   // value-factor storage
     constexpr int NT = G::NT, VEC = G::VEC, CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
@@ -334,14 +335,15 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     constexpr bool TOKEN = MODE != MODE_MERGE;
     constexpr bool LOG = MODE != MODE_EAGER;
     constexpr bool SPLIT = MODE == MODE_STEP_SPLIT;   // appends read ReplayPrep's coefficients
-    constexpr bool STEP = MODE == MODE_STEP || SPLIT;
-    constexpr bool HINTED = MODE == MODE_STEP;        // loads follow the host's live length
+    constexpr bool CONSEC = MODE == MODE_STEP_CONSEC; // slots slot0 + e, live lengths from the device
+    constexpr bool STEP = MODE == MODE_STEP || SPLIT || CONSEC;
+    constexpr bool HINTED = MODE == MODE_STEP || CONSEC;  // loads follow the host's live length, if given
     // Scalar or no decay: the replay coefficients' raw dot products are formed
     // while the log is staged (one key chunk per thread, DPP sums over the
     // chunk's CPE threads) and weighted e^{l'-Lam_i} where they are read, so
     // there is no separate coefficient pass or barrier.  Per-key decay needs
     // the snapshot chunk beside each key chunk and keeps the pass.
-    constexpr bool FC = (MODE == MODE_STEP || MODE == MODE_EAGER) && DECAY != DECAY_PER_KEY;
+    constexpr bool FC = (MODE == MODE_STEP || CONSEC || MODE == MODE_EAGER) && DECAY != DECAY_PER_KEY;
     constexpr int CPE = D / (16 / (int)sizeof(IT));   // 16-byte key chunks per log entry
     constexpr bool PERKEY = DECAY == DECAY_PER_KEY;
     constexpr bool SCALAR = DECAY == DECAY_SCALAR;
@@ -380,7 +382,9 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     // The launch geometry comes as leading scalar arguments (head counts, log
     // capacity, the q/k-head multiplier), which the build preloads into registers
     // before the block starts, so the block's slot word can be fetched at
-    // once.  The grid has one row per batch entry (blockIdx.y); along x run
+    // once.  So do the first slot of a launch of consecutive slots, the base
+    // and the live-length counters: such a block knows its slot and issues
+    // its counter load before any argument has been fetched from memory.  The grid has one row per batch entry (blockIdx.y); along x run
     // the entry's (v-head, value tile) units, numbered so that each XCD holds
     // a contiguous run of them.  No integer division: a wave issues one
     // instruction per four cycles, and a division by a run-time value costs
@@ -396,13 +400,19 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     const int g = (int)qk_head((uint32_t)h, gdiv);
     // the first v-head of its q/k group writes the group's key factor
     const bool kwriter = first_of_group((uint32_t)h, gdiv);
-    const uint32_t sword = p.slots[e];
-    // Every other argument the block reads is fetched now, with the slot
-    // word, in one batch: left to itself the compiler loads each where first
-    // used and waits for it before the next, a chain of round trips ahead of
-    // the first HBM access.
-    asm volatile("" ::"s"(p.base), "s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.nlog), "s"(p.q), "s"(p.k),
-                 "s"(p.v), "s"(p.lam), "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(sword));
+    // The slot word: computed in a launch of consecutive slots (which carries
+    // no live lengths from the host: the counter decides), else fetched with
+    // every other argument the block reads, in one batch: left to itself the
+    // compiler loads each where first used and waits for it before the next,
+    // a chain of round trips ahead of the first HBM access.
+    uint32_t sword;
+    if constexpr (CONSEC) {
+        sword = (slot0 + (uint32_t)e) | (kNoHint << kSlotBits);
+    } else {
+        sword = p.slots[e];
+        asm volatile("" ::"s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.lam),
+                     "s"(p.beta), "s"(p.out), "s"(p.coef), "s"(sword));
+    }
     const uint32_t slot = sword & kSlotMask;
     // Slot-head and slot-(q/k head) indices.  The host keeps P * H_v * N_V
     // below 2^31, so they and the (slot-head, tile) index fit 32 bits, and
@@ -427,9 +437,16 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     // stored yet): the scalar path answers in about half the time of a vector
     // load, and its wait does not hold the token loads, which a vector load's
     // in-order count would.  The scalar cache starts every launch empty, so it
-    // sees the previous launch's store.
+    // sees the previous launch's store.  A consecutive launch's block issues
+    // it before any argument has arrived (its slot, the counter and base
+    // pointers are in registers from the start), with the argument batch.
     int n_dev = 0;
-    if constexpr (HINTED) n_dev = ((const __attribute__((address_space(4))) int32_t *)(size_t)p.nlog)[shv];
+    if constexpr (HINTED) n_dev = ((const __attribute__((address_space(4))) int32_t *)(size_t)nlog)[shv];
+    if constexpr (CONSEC) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"s"(p.klog), "s"(p.ulog), "s"(p.lamlog), "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.lam),
+                     "s"(p.beta), "s"(p.out), "s"(p.coef));
+    }
 
     // ---- 1. every load of the block is issued before any is consumed: the
     //         token inputs (while the counter is in flight), the whole live
@@ -503,7 +520,7 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         const uint32_t hint = sword >> kSlotBits;
         n = hint == kNoHint ? min(max(__builtin_amdgcn_readfirstlane(n_dev), 0), C) : min((int)hint, C);
     } else if constexpr (LOG) {
-        n = p.nlog[shv];
+        n = nlog[shv];
     }
     if constexpr (MODE == MODE_MERGE) {
         if (n == 0) return;                             // empty log: nothing to materialize
@@ -656,7 +673,7 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
     // overlaps its arrival.  The base is value-tile major, [slot-head][NV][D][BV],
     // so the tile is one contiguous run: a thread reads tile rows rg + RG * j,
     // columns cg * VEC ..
-    const ST *tbase = reinterpret_cast<const ST *>(p.base) + (size_t)shv * (D * BV);
+    const ST *tbase = reinterpret_cast<const ST *>(base) + (size_t)shv * (D * BV);
     const uint32_t toff = (uint32_t)((rg * BV + cg * VEC) * sizeof(ST));
     constexpr uint32_t TROW = RG * BV * sizeof(ST);     // bytes between a thread's rows
     uint4 tile[RPT];
@@ -893,7 +910,7 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
                     if (tid == 0) p.lamlog[shC + n] = s_lp[0];
                 }
             }
-            if (tid == 0) p.nlog[shv] = merge ? 0 : n + 1;
+            if (tid == 0) nlog[shv] = merge ? 0 : n + 1;
         }
         __syncthreads();
 
@@ -955,7 +972,7 @@ dl_step_kernel(const int32_t H_v, const int32_t H_k, const int32_t C, const uint
         }
     }
     if constexpr (MODE == MODE_MERGE) {
-        if (tid == 0) p.nlog[shv] = 0;
+        if (tid == 0) nlog[shv] = 0;
     }
     if (!merge) return;
 
@@ -1132,6 +1149,7 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
     const uint32_t grp = (uint32_t)(p.H_v / p.H_k);
     if (p.H_v > 32768) return hipErrorInvalidValue;                   // qk_head exact below
     const uint32_t gdiv = (uint32_t)((0x80000000ull + grp - 1) / grp);
+#define LEAD p.slot0, p.base, p.nlog
     // narrow tiles with a scalar or no decay: decode and eager steps run the
     // one-barrier kernel where its lane layout fits (at least 4 key chunks per
     // entry, every thread owning tile rows, at most 32 bytes of value factor
@@ -1145,24 +1163,31 @@ static hipError_t launch_combo(int mode, const StepParams &p, size_t shmem, hipS
         if constexpr (NARROW)
             dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, false><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         else
-            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, LEAD, p);
         break;
     case MODE_EAGER:
         if constexpr (NARROW)
             dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, true><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
         else
-            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_EAGER><<<grid, block, 0, s>>>(p.H_v, p.H_k, p.C, gdiv, LEAD, p);
         break;
     case MODE_MERGE:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_MERGE><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, LEAD, p);
+        break;
+    case MODE_STEP_CONSEC:      // (narrow tiles read their slot words)
+        if constexpr (NARROW)
+            dl_small_kernel<D, BV, DECAY, DELTA, ST, IT, false><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
+        else
+            dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_CONSEC><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, LEAD, p);
         break;
     case MODE_STEP_SPLIT:
-        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, p);
+        dl_step_kernel<D, BV, DECAY, DELTA, ST, IT, MODE_STEP_SPLIT><<<grid, block, shmem, s>>>(p.H_v, p.H_k, p.C, gdiv, LEAD, p);
         break;
     default:
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+#undef LEAD
 }
 
 template <int D, int BV, int DECAY, bool DELTA>

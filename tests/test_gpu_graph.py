@@ -318,3 +318,80 @@ def test_serving_pool_steps_with_assignments_in_a_graph():
     del g
     pool.close()
     assert st_e.value <= 2e-2
+
+
+@pytest.mark.parametrize("idx,L,value_tile", [(2, 4, 128), (5, 4, 128), (3, 4, 0), (4, 4, 0), (5, 4, 0),
+                                                 (4, 1, 0), (2, 1, 128)])
+def test_consecutive_and_gathered_slots(idx, L, value_tile):
+    """Launches whose slots are consecutive name their first slot instead of
+    carrying slot words (the blocks then compute their slots).  Consecutive
+    runs that start past slot 0, gathered sets and single slots, decoded
+    directly and from a replayed graph, merged and flushed, all follow the
+    oracle; L = 1 runs the eager kernel through the same launches."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    base = CONFIGS[idx]
+    cfg = small_variant(base, batch=3, steps=6, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=L,
+                        name=f"consecutive_{base.name}", random_slots=False, replace_per_step=0,
+                        ragged_fill=False, num_slots=10)
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    P = cfg.num_slots
+    pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, max_batch=P, value_tile=value_tile)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    sets = [np.array(s, dtype=np.int32) for s in ([4, 5, 6], [8, 1, 5], [7, 8, 9], [2, 3, 4], [6, 0, 9])]
+    steps = [wl.step_inputs(d) for d in wl.main_steps()]
+    tol = 2e-2 if cfg.state_dtype == "bf16" else 1e-4
+    say(f"[gpu] consecutive / gathered slots: {cfg.describe()} value_tile={value_tile}")
+    err = RelL2()
+    step_fn = pool.eager_step if L == 1 else pool.decode_step
+
+    def run(s, slots, out=None, check=True):
+        o = step_fn(slots, to_dev(s.q, it), to_dev(s.k, it), to_dev(s.v, it),
+                    to_dev(s.lam, torch.float32), to_dev(s.beta, torch.float32), out)
+        if check:
+            _, o_ref = E.step(slots, s.q, s.k, s.v, s.lam, s.beta)
+            err.add(o.cpu().numpy(), o_ref)
+        return o
+
+    for k, s in enumerate(steps):                  # direct launches
+        run(s, sets[k % len(sets)])
+    torch.cuda.synchronize()
+    say(f"[gpu]   direct: out rel-L2 {err.value:.3e}")
+    # captured: one step per slot set, then replayed with checks between
+    dev = [dict(q=to_dev(s.q, it), k=to_dev(s.k, it), v=to_dev(s.v, it), lam=to_dev(s.lam, torch.float32),
+                beta=to_dev(s.beta, torch.float32),
+                out=torch.empty((cfg.batch, cfg.H_v, cfg.d), dtype=torch.float32, device="cuda"))
+           for s in steps[:len(sets)]]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d, slots in zip(dev, sets):
+            step_fn(slots, d["q"], d["k"], d["v"], d["lam"], d["beta"], d["out"])
+        if L > 1:
+            pool.merge(np.array([7, 8, 9], dtype=np.int32))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for s, d, slots in zip(steps, dev, sets):
+            _, o_ref = E.step(slots, s.q, s.k, s.v, s.lam, s.beta)
+            err.add(d["out"].cpu().numpy(), o_ref)
+        say(f"[gpu]   replay {rep}: out rel-L2 {err.value:.3e}")
+    if L > 1:
+        n_dev = pool.device_log_len()
+        assert np.all(n_dev[7:10] == 0)            # the recorded merge emptied them at every replay
+    pool.flush_all()
+    torch.cuda.synchronize()
+    se = RelL2()
+    se.add(pool.read_base(ids).float().cpu().numpy(), E.states(ids))
+    say(f"[gpu]   out rel-L2 {err.value:.3e}, state rel-L2 {se.value:.3e}")
+    del g
+    pool.close()
+    assert err.value <= tol and se.value <= tol
