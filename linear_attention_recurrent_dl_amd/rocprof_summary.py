@@ -4,6 +4,7 @@
     python -m linear_attention_recurrent_dl_amd.rocprof_summary pmc    <results.db | counter_collection.csv> COUNTER
     python -m linear_attention_recurrent_dl_amd.rocprof_summary traffic FETCH_DB WRITE_DB KERNEL_SUBSTR COPY_BYTES [OUT.json|-] [LAST_N]
     python -m linear_attention_recurrent_dl_amd.rocprof_summary tail   <kernel_trace.csv> KERNEL_SUBSTR N
+    python -m linear_attention_recurrent_dl_amd.rocprof_summary phases <kernel_trace.csv> KERNEL_SUBSTR R L REPS
 
 ``trace`` prints count / average / min / max duration per kernel name;
 ``pmc`` prints, per kernel name, the average value of COUNTER per dispatch and
@@ -16,6 +17,13 @@ size, over all its dispatches or its last LAST_N (CSV input).  ``tail`` splits t
 KERNEL_SUBSTR, in start order, into all but the last N and the last N, and
 prints count and average duration of each part and the median start-to-start
 period of the last N (a timed graph replay is the last dispatches of a run).
+``phases`` sorts the last REPS x R x L dispatches of that kernel (REPS timed
+replays of a graph of whole merge cycles over R pools decoded in turn, pool
+t mod R at step t, every slot of a pool in the same phase) by the live-log
+length n each one started from: within a replay, every R-th dispatch belongs
+to one pool, its longest dispatch is that pool's merge (n = L - 1), and the
+dispatch k places after it starts from n = k - 1.  Prints the average duration
+per n.
 Works on the SQLite database rocprofv3 writes by default (``*_results.db``)
 and on its CSV output (``tail``: CSV only).
 """
@@ -66,6 +74,27 @@ def trace_tail(path: str, sub: str, n: int):
     starts = [s for s, _ in tail]
     per = sorted(b - a for a, b in zip(starts, starts[1:]))
     return len(head), avg(head), len(tail), avg(tail), (per[len(per) // 2] if per else 0.0)
+
+
+def trace_phases(path: str, sub: str, R: int, L: int, reps: int):
+    """{n: [duration ns]} of the last reps * R * L dispatches of one kernel."""
+    spans = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if sub in (r.get("Kernel_Name") or ""):
+                spans.append((float(r["Start_Timestamp"]), float(r["End_Timestamp"])))
+    spans.sort()
+    per = R * L
+    spans = spans[-reps * per:]
+    by = defaultdict(list)
+    for rep in range(len(spans) // per):
+        blk = spans[rep * per:(rep + 1) * per]
+        for p in range(R):
+            durs = [e - s for s, e in blk[p::R]]
+            km = max(range(len(durs)), key=lambda k: durs[k])
+            for k, dur in enumerate(durs):
+                by[L - 1 if k == km else (k - km - 1) % L].append(dur)
+    return by
 
 
 def pmc_dispatches(path: str, counter: str):
@@ -209,6 +238,12 @@ def main(argv=None) -> int:
         print(f"kernel containing: {argv[2]}")
         print(f"first {nh} dispatches: avg {ah / 1e3:.3f} us")
         print(f"last {nt} dispatches: avg {at / 1e3:.3f} us, median start-to-start {pt / 1e3:.3f} us")
+    elif mode == "phases":
+        by = trace_phases(path, argv[2], int(argv[3]), int(argv[4]), int(argv[5]))
+        print(f"kernel containing: {argv[2]}")
+        print(f"{'n':>3s} {'dispatches':>10s} {'avg_us':>9s}")
+        for n in sorted(by):
+            print(f"{n:3d} {len(by[n]):10d} {sum(by[n]) / len(by[n]) / 1e3:9.3f}")
     elif mode == "traffic":
         import json
         last = int(argv[6]) if len(argv) > 6 else 0

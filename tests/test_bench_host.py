@@ -162,3 +162,33 @@ def test_traffic_averages_the_most_dispatched_matching_kernel(tmp_path):
     assert t["kernel"] == dec and t["dispatches"] == 64
     assert t["hbm_fetch_bytes_per_launch"] == 100.0 * 1024 * 2
     assert t["hbm_write_bytes_per_launch"] == 10.0 * 1024
+
+
+def test_trace_phases_sorts_dispatches_by_live_length(tmp_path):
+    # two timed replays of 3 pools x L = 4 steps, pools decoded in turn; pool p
+    # starts each replay at phase p (its merge is its (3 - p)-th dispatch),
+    # and a dispatch starting from n entries lasts 10 + n (merge: 100) ns;
+    # earlier dispatches of the kernel (warm-up) and other kernels are ignored
+    from linear_attention_recurrent_dl_amd.rocprof_summary import trace_phases
+    R, L = 3, 4
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for _ in range(5):                             # warm-up dispatches of the same kernel
+        rows.append(f'"k<1>",{t},{t + 7}')
+        t += 1000
+    for _ in range(2):
+        for step in range(R * L):
+            p, k = step % R, step // R
+            n = (p + k) % L
+            rows.append(f'"other",{t},{t + 5}')
+            t += 1000
+            rows.append(f'"k<1>",{t},{t + (100 if n == L - 1 else 10 + n)}')
+            t += 1000
+    path = tmp_path / "tr.csv"
+    path.write_text("\n".join(rows) + "\n")
+    by = trace_phases(str(path), "k<1>", R, L, 2)
+    assert sorted(by) == [0, 1, 2, 3]
+    assert all(len(v) == 2 * R for v in by.values())
+    assert by[3] == [100] * (2 * R)
+    for n in range(L - 1):
+        assert by[n] == [10 + n] * (2 * R)
