@@ -164,12 +164,21 @@ enum { DL_BUF_BASE = 0, DL_BUF_KLOG, DL_BUF_ULOG, DL_BUF_LAMLOG, DL_BUF_NLOG, DL
 
 typedef struct dl_pool dl_pool;
 
-/* Byte size of each pool buffer, indexed by DL_BUF_*.  Host only. */
+/* Byte size of each pool buffer, indexed by DL_BUF_*: the physical state of
+ * num_slots slots ([DL] physical-state list: dense base, log entries K_i, U_i,
+ * Lambda_i, live length) in the layouts above, and the split-replay
+ * coefficient buffer.  Host only; allocates nothing.  Returns
+ * DL_ERR_INVALID_ARG / DL_ERR_UNSUPPORTED for a descriptor that dl_pool_create
+ * would refuse (same checks), else DL_OK with bytes_out filled. */
 int dl_pool_sizes(const dl_pool_desc *desc, size_t bytes_out[DL_NUM_BUFS]);
 
-/* Create a pool over caller-owned buffers.  Every slot starts with an empty
+/* Create a pool over caller-owned buffers: the slot pool of [DL]'s
+ * serving-integration section (per-slot state with its own log counter; the
+ * host handle keeps the merge schedule).  Every slot starts with an empty
  * log (nlog is zeroed here, synchronously); the base is left as the caller
- * wrote it -- use dl_slot_assign to set it.  buffers == NULL creates a
+ * wrote it -- use dl_slot_assign to set it.  Errors: the descriptor checks of
+ * dl_pool_sizes, a NULL or non-16-byte-aligned buffer whose size is not 0
+ * (DL_ERR_INVALID_ARG), DL_ERR_HIP if zeroing nlog fails; *out is NULL then.  buffers == NULL creates a
  * host-only pool: every call validates and advances the host mirror exactly as
  * it would on the device but enqueues nothing (for bookkeeping checks without
  * a GPU).  *out receives the handle. */
@@ -274,8 +283,10 @@ int dl_eager_step(dl_pool *pool, int32_t B, const int32_t *slot_ids,
  * the listed slots becomes 0. */
 int dl_merge(dl_pool *pool, int32_t n, const int32_t *slot_ids, void *stream);
 
-/* dl_merge over every slot whose log is not empty; afterwards every log is
- * empty and every base is its slot's logical state.  Idempotent.  The host
+/* dl_merge over every slot whose log is not empty ([DL] Algorithm 1's merge
+ * for the whole pool, e.g. before the bases are read back or handed to another
+ * consumer); afterwards every log is empty and every base is its slot's
+ * logical state.  Idempotent.  The host
  * mirror selects the slots while it follows the device; once any call on the
  * pool has been recorded into a graph (including this one), replays may have
  * moved the device counters without it, and every slot of the pool is
