@@ -320,14 +320,18 @@ def test_serving_pool_steps_with_assignments_in_a_graph():
     assert st_e.value <= 2e-2
 
 
-@pytest.mark.parametrize("idx,L,value_tile", [(2, 4, 128), (5, 4, 128), (3, 4, 0), (4, 4, 0), (5, 4, 0),
-                                                 (4, 1, 0), (2, 1, 128)])
-def test_consecutive_and_gathered_slots(idx, L, value_tile):
+@pytest.mark.parametrize("idx,L,value_tile,in_dtype", [(2, 4, 128, None), (5, 4, 128, None), (3, 4, 0, None),
+                                                          (4, 4, 0, None), (5, 4, 0, None), (4, 1, 0, None),
+                                                          (2, 1, 128, None), (1, 4, 0, "bf16")])
+def test_consecutive_and_gathered_slots(idx, L, value_tile, in_dtype):
     """Launches whose slots are consecutive name their first slot instead of
     carrying slot words (the blocks then compute their slots).  Consecutive
     runs that start past slot 0, gathered sets and single slots, decoded
     directly and from a replayed graph, merged and flushed, all follow the
-    oracle; L = 1 runs the eager kernel through the same launches."""
+    oracle; L = 1 runs the eager kernel through the same launches.  (Plain LA
+    at d = 16 with bf16 inputs has two key chunks per entry, too few for the
+    one-barrier narrow kernel: it runs the narrow-tile staging of the general
+    decode kernel.)"""
     import torch
 
     import linear_attention_recurrent_dl_amd as dl
@@ -335,9 +339,10 @@ def test_consecutive_and_gathered_slots(idx, L, value_tile):
     from oracle import EagerPool, RelL2
 
     base = CONFIGS[idx]
+    extra = {"in_dtype": in_dtype} if in_dtype else {}
     cfg = small_variant(base, batch=3, steps=6, H_v=4, H_k=2 if base.H_k < base.H_v else 4, L=L,
                         name=f"consecutive_{base.name}", random_slots=False, replace_per_step=0,
-                        ragged_fill=False, num_slots=10)
+                        ragged_fill=False, num_slots=10, **extra)
     wl = Workload(cfg)
     st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
     P = cfg.num_slots
