@@ -400,3 +400,57 @@ def test_consecutive_and_gathered_slots(idx, L, value_tile, in_dtype):
     del g
     pool.close()
     assert err.value <= tol and se.value <= tol
+
+
+def test_consecutive_slots_split_over_launches():
+    """A recorded call over more slots than one launch carries is split into
+    launches, each of which decides on its own whether its slots are
+    consecutive: a run of 1100 slots (three consecutive launches, the second
+    and third starting past slot 0) and a gathered permutation of the same
+    slots, replayed, against the oracle (plain LA, d = 16, L = 4, bf16 inputs:
+    the general decode kernel, which takes the first slot of a consecutive
+    launch)."""
+    import torch
+
+    import linear_attention_recurrent_dl_amd as dl
+    from gpu_harness import TDT, say, to_dev
+    from oracle import EagerPool, RelL2
+
+    base = CONFIGS[1]
+    P = 1100
+    cfg = small_variant(base, batch=P, steps=4, L=4, name="consecutive_split", num_slots=P, in_dtype="bf16")
+    assert dl.dl_launch_slot_limit() < P
+    wl = Workload(cfg)
+    st, it = TDT[cfg.state_dtype], TDT[cfg.in_dtype]
+    pool = dl.DeltaLogPool(P, cfg.H_v, cfg.H_k, cfg.d, cfg.L, cfg.decay, cfg.update, cfg.state_dtype,
+                           cfg.in_dtype, max_batch=P)
+    ids = np.arange(P, dtype=np.int32)
+    pool.assign(ids, to_dev(wl.init_base(ids), st))
+    E = EagerPool(ids, cfg.H_v, cfg.d, cfg.d, cfg.decay, cfg.update, init=wl.init_base(ids))
+    perm = np.random.default_rng(7).permutation(P).astype(np.int32)
+    sets = [ids, perm, ids, perm]
+    steps = [wl.step_inputs(d) for d in wl.main_steps()]
+    say(f"[gpu] consecutive launches split: {cfg.describe()}")
+    dev = [dict(q=to_dev(s.q, it), k=to_dev(s.k, it), v=to_dev(s.v, it),
+                out=torch.empty((P, cfg.H_v, cfg.d), dtype=torch.float32, device="cuda")) for s in steps]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d, slots in zip(dev, sets):
+            pool.decode_step(slots, d["q"], d["k"], d["v"], None, None, d["out"])
+    torch.cuda.synchronize()
+    err = RelL2()
+    for rep in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        for s, d, slots in zip(steps, dev, sets):
+            _, o_ref = E.step(slots, s.q, s.k, s.v, None, None)
+            err.add(d["out"].cpu().numpy(), o_ref)
+    pool.flush_all()
+    torch.cuda.synchronize()
+    se = RelL2()
+    se.add(pool.read_base(ids).float().cpu().numpy(), E.states(ids))
+    say(f"[gpu]   out rel-L2 {err.value:.3e}, state rel-L2 {se.value:.3e}")
+    del g
+    pool.close()
+    assert err.value <= 1e-4 and se.value <= 1e-4
